@@ -1,0 +1,123 @@
+/*
+ * q4.h -- C ABI of the MI355X (gfx950) weight-only 4-bit group-quantized
+ * matrix-vector / matrix-matrix product and of the quantizer that feeds it.
+ *
+ * The method: weights are quantized symmetrically to 4 bits in groups of 32
+ * consecutive input elements, and dequantized through a 16-entry lookup
+ * table inside the product (QORA-4B forum article, section on quantization
+ * and memory management; QORA-LLM-0.8B model card, "Weight Format" and the
+ * Q4 GEMV row of "AVX-512 SIMD Acceleration").  The pages name the scheme but
+ * fix no bit layout; the layout below is the one this library defines.
+ *
+ * Data layout (all tensors dense, row-major, no strides):
+ *   W       fp32    [n, k]      weights, one output feature per row
+ *   packed  uint8   [n, k/2]    byte i of row r holds element 2i of the row in
+ *                               its low nibble and element 2i+1 in its high
+ *                               nibble, each stored as q + 8 (0..15)
+ *   scales  fp16    [n, k/32]   one scale per group of 32 elements, carried
+ *                               as raw IEEE binary16 bit patterns (uint16_t)
+ *   x       fp16    [m, k]      activations, raw binary16 bits
+ *   y       fp32    [m, n]      y[i][r] = sum_j s[r][j] * sum_t x[i][32j+t] * q[r][32j+t]
+ *
+ * Quantization of one group g (32 fp32 values w):
+ *   amax = max |w|                       (exact)
+ *   s    = fp16_rne( amax / 7.0f )       (IEEE fp32 division, then round to
+ *                                         nearest-even binary16)
+ *   q    = 0                             if s == 0
+ *          clamp(rne(w / float(s)), -8, 7) otherwise (IEEE fp32 division of w
+ *                                         by the stored fp16 scale widened to
+ *                                         fp32, rounded half to even)
+ * The result is unique: every implementation must produce identical bytes.
+ *
+ * Common argument rules for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or keeps them after the call returns, and uses no
+ *     workspace.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Work is enqueued asynchronously; the caller keeps inputs alive and
+ *     unmodified until the stream has completed it.  Outputs are overwritten
+ *     (never accumulated into) and must not alias any input.
+ *   - Shapes: n >= 1, k >= 32, k % 32 == 0, n <= 2^31 - 1, k <= 2^24, and
+ *     n * k <= 2^40; otherwise Q4_ERR_SHAPE.
+ *   - Alignment: x and packed 16-byte aligned, w and y 4-byte aligned,
+ *     scales 2-byte aligned; otherwise Q4_ERR_ALIGN.
+ *   - Validation happens on the host, synchronously, before anything is
+ *     enqueued; on any error nothing is launched.  A launch failure reported
+ *     by the HIP runtime maps to Q4_ERR_LAUNCH.  Faults raised asynchronously
+ *     by the device surface at the caller's next synchronisation, as with any
+ *     HIP work.  No C++ exception and no abort crosses this interface.
+ *   - Results are deterministic: no atomics, bit-identical from run to run.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1
+#define Q4_GROUP 32
+
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,    /* a required pointer is NULL                        */
+    Q4_ERR_SHAPE = 2,   /* m, n or k outside the documented ranges            */
+    Q4_ERR_ALIGN = 3,   /* a pointer breaks the alignment rule                */
+    Q4_ERR_LAUNCH = 4,  /* the HIP runtime refused or failed the launch       */
+    Q4_ERR_DEVICE = 5   /* no usable gfx950 device is current                 */
+} q4_status;
+
+/* Version of this interface; equals Q4_ABI_VERSION of the built library. */
+int q4_abi_version(void);
+
+/* Static, NUL-terminated English name of a status code (never NULL). */
+const char* q4_status_str(q4_status status);
+
+/*
+ * q4_quantize -- symmetric 4-bit group quantization of a weight matrix.
+ * Follows the Q4 format the QORA pages describe (4-bit, symmetric, groups of
+ * 32) with the bit-level rules stated at the top of this header.
+ *   w       [in]  fp32 [n, k], device
+ *   packed  [out] uint8 [n, k/2], device
+ *   scales  [out] fp16 bits [n, k/32], device
+ * Precondition (not checked, outside the contract): every w is finite and
+ * |w| < 7 * 65520, so that every scale is a finite binary16.
+ */
+q4_status q4_quantize(const float* w, uint8_t* packed, uint16_t* scales,
+                      int64_t n, int64_t k, void* stream);
+
+/*
+ * q4_gemv -- decode-time product y = x * dequant(W)^T for 1 <= m <= 8 rows of
+ * activations (one token, or a handful such as a speculative-verify batch).
+ * This is the Q4 GEMV that the QORA engines run for every projection and for
+ * the 248,320-row LM head (QORA-LLM-0.8B model card, "AVX-512 SIMD
+ * Acceleration" and "Weight Format"; QORA-4B article, quantization section).
+ *   x       [in]  fp16 bits [m, k], device
+ *   packed  [in]  uint8 [n, k/2], device (layout above)
+ *   scales  [in]  fp16 bits [n, k/32], device
+ *   y       [out] fp32 [m, n], device
+ * m outside 1..8 -> Q4_ERR_SHAPE (use q4_gemm).
+ * Accuracy: fp16 x times exact integers, fp32 accumulation, group scale
+ * applied in fp32 after each 32-element dot product.
+ */
+q4_status q4_gemv(const uint16_t* x, const uint8_t* packed,
+                  const uint16_t* scales, float* y,
+                  int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * q4_gemm -- prefill product, same arguments and semantics as q4_gemv, for
+ * any m in 1 .. 2^31-1 (tuned for m >= 16): all projections of a token batch
+ * computed at once, as in the QORA-4B article's GPU prefill section and the
+ * batched prefill of the QORA-LLM-0.8B card ("Performance").
+ */
+q4_status q4_gemm(const uint16_t* x, const uint8_t* packed,
+                  const uint16_t* scales, float* y,
+                  int64_t m, int64_t n, int64_t k, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */
