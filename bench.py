@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 Q4 group-quantized GEMV/GEMM path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+
+Prints ONE JSON line.  The workload is the 0.8B-shaped decode set at M = 1
+(hidden 1024: DeltaNet q/k/v 3 x 2048 rows, attention q 2048, k 512, v 512,
+LM head 248,320 rows), weights ~ N(0, 0.02^2) quantized on the GPU, x ~ N(0,1)
+in fp16.  One step is one decode pass: the seven q4_gemv products on the same
+x, replayed from a HIP graph.  The step rotates through enough copies of the
+quantized weights (>= 1 GiB) that no step finds its weights in the 256 MB
+Infinity Cache: the figure is HBM-bound throughput, not cache bandwidth.
+
+value    = algorithmic bytes of one step / step time (GB/s); algorithmic bytes
+           of one product = n*k/2 (codes) + n*k/16 (fp16 scales) + 2*m*k (x)
+           + 4*m*n (y)
+roofline = the dominant kernel (the LM-head GEMV): its algorithmic bytes per
+           launch / its average launch duration from HIP events, against the
+           8 TB/s HBM3E peak
+detail   = the other halves of the hot path measured in the same run: the
+           M = 512 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s dense fp16
+           MFMA peak) and the quantizer (GB/s); --all adds the 4B decode set,
+           the M = 8 verify LM head and the M = 16/128/2048 prefill GEMMs
+cpu_baseline = the CPU oracle (plain C, fp64 product) on a bounded sample of
+           the same decode set, GB/s over the same algorithmic bytes
+
+--rocprof-summary TRACE.csv groups a rocprofv3 kernel trace by kernel and
+grid size (the LM head and the projections run the same kernel at different
+grid sizes) and prints average durations.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP16_MFMA_PEAK_TFS = 2500.0    # MI355X dense fp16 MFMA
+ROTATE_BYTES = 1 << 30         # rotate through >= 1 GiB of weight copies
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lmhead_08b_traffic.json")
+KERNEL_SOURCES = ["q4_group_quantized_amd/csrc/q4_gemv.hip",
+                  "q4_group_quantized_amd/csrc/q4_device.hpp"]
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 trace summary
+# --------------------------------------------------------------------------
+
+def rocprof_summary(path: str) -> None:
+    import csv
+    groups = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            name = row.get("Kernel_Name", "?")
+            grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "?"
+            dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            groups.setdefault((name, grid), []).append(dur)
+    print("%-10s %-8s %-12s %-12s %s" % ("grid", "calls", "avg_ns", "min_ns", "kernel"))
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) < 90 else name[:87] + "..."
+        print("%-10s %-8d %-12.0f %-12d %s" % (grid, len(d), sum(d) / len(d), min(d), short))
+
+
+# --------------------------------------------------------------------------
+# GPU helpers
+# --------------------------------------------------------------------------
+
+class Product:
+    """One quantized matrix resident in HBM, with rotation copies and an output."""
+
+    def __init__(self, torch, q4, mat, m, x, copies, outliers=False):
+        import q4_inputs as qi
+        self.mat, self.m = mat, m
+        w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id, wide_groups=mat.wide_groups)
+        wg = torch.from_numpy(w).cuda()
+        del w
+        packed, scales = q4.q4_quantize(wg)
+        del wg
+        self.copies = [(packed, scales)] + [(packed.clone(), scales.clone())
+                                             for _ in range(copies - 1)]
+        self.x = x
+        self.y = torch.empty((m, mat.n), dtype=torch.float32, device=x.device)
+        self.bytes = qi.workload_bytes(m, mat.n, mat.k)
+        self.flops = qi.workload_flops(m, mat.n, mat.k)
+        self.weight_bytes = packed.numel() + scales.numel() * 2
+
+    def args(self, c):
+        p, s = self.copies[c % len(self.copies)]
+        return (self.x.data_ptr(), p.data_ptr(), s.data_ptr(), self.y.data_ptr(),
+                self.m, self.mat.n, self.mat.k)
+
+
+def launch(lib, fn, args, stream):
+    st = getattr(lib, fn)(*args, stream)
+    if st != 0:
+        raise RuntimeError("%s failed with status %d" % (fn, st))
+
+
+def time_launches(torch, lib, fn, prod, iters, stream_handle, per_launch_events):
+    """Average duration (s) of `iters` launches rotating through the copies."""
+    torch.cuda.synchronize()
+    if per_launch_events:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for i in range(iters):
+            evs[i][0].record()
+            launch(lib, fn, prod.args(i), stream_handle)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / iters / 1e3
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        launch(lib, fn, prod.args(i), stream_handle)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters / 1e3
+
+
+def decode_set(torch, q4, lib, workload, warmup, steps):
+    """Build a decode set, capture one graph per weight copy, time K steps."""
+    import q4_inputs as qi
+    mats = [mat for mat, _ in workload.cases]
+    k = mats[0].k
+    x = torch.from_numpy(qi.activations(1, k, outliers=workload.outliers)).cuda()
+    set_weight_bytes = sum(m.n * m.k // 2 + m.n * (m.k // 32) * 2 for m in mats)
+    copies = max(2, math.ceil(ROTATE_BYTES / set_weight_bytes))
+    log("%s: %d matrices, %.1f MB of weights, %d copies" % (
+        workload.key, len(mats), set_weight_bytes / 1e6, copies))
+    prods = [Product(torch, q4, mat, 1, x, copies) for mat in mats]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    # eager reference results of copy 0, then one graph per copy
+    for p in prods:
+        launch(lib, "q4_gemv", p.args(0), sh)
+    torch.cuda.synchronize()
+    eager = [p.y.clone() for p in prods]
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            h = torch.cuda.current_stream().cuda_stream
+            for p in prods:
+                launch(lib, "q4_gemv", p.args(c), h)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    # every copy's graph must reproduce the eager result bit for bit
+    for c in range(copies):
+        for p in prods:
+            p.y.zero_()
+        torch.cuda.synchronize()
+        graphs[c].replay()
+        torch.cuda.synchronize()
+        for p, e in zip(prods, eager):
+            if not torch.equal(p.y, e):
+                raise RuntimeError("graph replay of copy %d differs from eager run" % c)
+
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        graphs[i % copies].replay()
+    b.record()
+    torch.cuda.synchronize()
+    step_s = a.elapsed_time(b) / steps / 1e3
+    set_bytes = sum(p.bytes for p in prods)
+    per = []
+    for p in prods:
+        t = time_launches(torch, lib, "q4_gemv", p, max(50, 2 * copies), sh, True)
+        per.append({"matrix": p.mat.name, "n": p.mat.n, "k": p.mat.k, "us": round(t * 1e6, 3),
+                    "GB_s": round(p.bytes / t / 1e9, 1),
+                    "hbm_frac": round(p.bytes / t / 1e9 / HBM_PEAK_GBS, 4)})
+    return {"prods": prods, "step_s": step_s, "set_bytes": set_bytes, "per_matrix": per,
+            "copies": copies}
+
+
+def gemm_case(torch, q4, lib, mat, m, outliers, iters):
+    import q4_inputs as qi
+    x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
+    copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 9 // 16))) if m <= 8 else 1
+    p = Product(torch, q4, mat, m, x, copies)
+    fn = "q4_gemv" if m <= 8 else "q4_gemm"
+    sh = torch.cuda.current_stream().cuda_stream
+    time_launches(torch, lib, fn, p, 5, sh, False)
+    t = time_launches(torch, lib, fn, p, iters, sh, False)
+    out = {"matrix": mat.name, "m": m, "n": mat.n, "k": mat.k, "fn": fn, "us": round(t * 1e6, 3),
+           "TFLOP_s": round(p.flops / t / 1e12, 2),
+           "mfma_frac": round(p.flops / t / 1e12 / FP16_MFMA_PEAK_TFS, 4),
+           "GB_s": round(p.bytes / t / 1e9, 1),
+           "hbm_frac": round(p.bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del p
+    torch.cuda.empty_cache()
+    return out
+
+
+def quantize_rate(torch, q4, mat, iters):
+    import q4_inputs as qi
+    w = torch.from_numpy(qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)).cuda()
+    packed = torch.empty((mat.n, mat.k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((mat.n, mat.k // 32), dtype=torch.float16, device=w.device)
+    q4.q4_quantize(w, out=(packed, scales))
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        q4.q4_quantize(w, out=(packed, scales))
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / iters / 1e3
+    nbytes = mat.n * mat.k * 4 + mat.n * mat.k // 2 + mat.n * (mat.k // 32) * 2
+    del w, packed, scales
+    torch.cuda.empty_cache()
+    return {"matrix": mat.name, "n": mat.n, "k": mat.k, "us": round(t * 1e6, 2),
+            "GB_s": round(nbytes / t / 1e9, 1),
+            "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode set
+# --------------------------------------------------------------------------
+
+def cpu_baseline(workload, budget_s=12.0):
+    import oracle
+    import q4_inputs as qi
+    o = oracle.get()
+    mats = [mat for mat, _ in workload.cases]
+    k = mats[0].k
+    x = qi.activations(1, k, outliers=workload.outliers)
+    total_t, total_b, parts = 0.0, 0, []
+    for mat in mats:
+        rows = mat.n
+        if mat.n > 8192:
+            # calibrate on 2048 rows, then size the sample to the remaining budget
+            w = qi.weight_rows(mat.n, mat.k, 0, 2048, tensor_id=mat.tensor_id)
+            p, s = o.quantize(w)
+            t0 = time.perf_counter()
+            o.matmul(x, p, s)
+            dt = time.perf_counter() - t0
+            rows = int(min(mat.n, max(2048, 2048 * max(budget_s - total_t, 1.0) / max(dt, 1e-6))))
+        w = qi.weight_rows(mat.n, mat.k, 0, rows, tensor_id=mat.tensor_id)
+        p, s = o.quantize(w)
+        t0 = time.perf_counter()
+        o.matmul(x, p, s)
+        dt = time.perf_counter() - t0
+        total_t += dt
+        total_b += qi.workload_bytes(1, rows, mat.k)
+        parts.append("%s %d/%d rows" % (mat.name, rows, mat.n))
+    return {"value": round(total_b / total_t / 1e9, 3), "unit": "GB/s", "cores": o.threads(),
+            "kind": "oracle",
+            "sample": "oracle q4o_matmul (fp64) on the decode set at M=1: " + ", ".join(parts)
+                      + "; %.1f s of CPU time" % total_t}
+
+
+# --------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--all", action="store_true", help="also time the other configurations")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rocprof-summary", metavar="KERNEL_TRACE_CSV")
+    args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this Q4 GEMV/GEMM path runs on one GPU; --gpus %d is not supported "
+              "(sharding is described in DESIGN.md, not built)" % max(args.gpus, world),
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import q4_group_quantized_amd as q4
+    import q4_inputs as qi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    lib = q4.load()
+    torch.cuda.set_device(0)
+
+    wl = qi.WORKLOADS["decode_08b"]
+    log("decode set 0.8B: building")
+    ds = decode_set(torch, q4, lib, wl, args.warmup, args.steps)
+    value = ds["set_bytes"] / ds["step_s"] / 1e9
+
+    # dominant kernel: the LM-head GEMV, per-launch HIP events (cold, rotating copies)
+    lm = ds["prods"][-1]
+    sh = torch.cuda.current_stream().cuda_stream
+    lm_t = time_launches(torch, lib, "q4_gemv", lm, max(200, 4 * ds["copies"]), sh, True)
+    achieved = lm.bytes / lm_t / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "q4_gemv LM head m=1 n=248320 k=1024",
+                "bytes_per_launch": lm.bytes, "avg_launch_us": round(lm_t * 1e6, 3)}
+    del ds["prods"], lm
+    torch.cuda.empty_cache()
+
+    detail = {"decode_08b_per_matrix": ds["per_matrix"], "rotation_copies": ds["copies"]}
+    log("prefill GEMM M=512")
+    detail["gemm_m512"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
+    log("quantize 0.8B LM head")
+    detail["quantize_lm_head_08b"] = quantize_rate(torch, q4, qi.DECODE_08B[-1], 10)
+    if args.all:
+        log("decode set 4B")
+        d4 = decode_set(torch, q4, lib, qi.WORKLOADS["decode_4b"], args.warmup, args.steps)
+        detail["decode_4b"] = {"GB_s": round(d4["set_bytes"] / d4["step_s"] / 1e9, 1),
+                               "us_per_step": round(d4["step_s"] * 1e6, 2),
+                               "per_matrix": d4["per_matrix"]}
+        del d4
+        torch.cuda.empty_cache()
+        for m in (16, 128, 2048):
+            log("prefill GEMM M=%d" % m)
+            mat = qi.PREFILL_4B if m != 2048 else qi.PREFILL_4B_WIDE
+            detail["gemm_m%d" % m] = gemm_case(torch, q4, lib, mat, m, m != 2048, 50)
+        log("verify LM head M=8")
+        detail["verify_m8_lm_head"] = gemm_case(torch, q4, lib, qi.LM_HEAD_4B_WIDE, 8, False, 50)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(wl)
+
+    out = {
+        "metric": "Q4 GEMV HBM GB/s (% of peak) at M=1; Q4 GEMM TFLOP/s (% MFMA peak) M=512",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ds["step_s"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xq4->f32",
+        "data": "synthetic",
+        "config": {"workload": "0.8B-shaped Q4 decode set, M=1, K=1024 (7 GEMVs incl. "
+                               "248320-row LM head), weights rotated over %d copies"
+                               % ds["copies"],
+                   "m": 1, "k": 1024, "n": [mat.n for mat, _ in wl.cases],
+                   "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -39,7 +39,7 @@
  *     (never accumulated into) and must not alias any input.
  *   - Shapes: n >= 1, k >= 32, k % 32 == 0, n <= 2^31 - 1, k <= 2^24, and
  *     n * k <= 2^40; otherwise Q4_ERR_SHAPE.
- *   - Alignment: x and packed 16-byte aligned, w and y 4-byte aligned,
+ *   - Alignment: x, packed and w 16-byte aligned, y 4-byte aligned,
  *     scales 2-byte aligned; otherwise Q4_ERR_ALIGN.
  *   - Validation happens on the host, synchronously, before anything is
  *     enqueued; on any error nothing is launched.  A launch failure reported

@@ -56,7 +56,12 @@ class Oracle:
         lib.q4o_quantize.restype = ctypes.c_int
         lib.q4o_matmul.argtypes = [p, p, p, i64, i64, i64, p, p]
         lib.q4o_matmul.restype = ctypes.c_int
+        lib.q4o_threads.argtypes = []
+        lib.q4o_threads.restype = ctypes.c_int
         self.lib = lib
+
+    def threads(self) -> int:
+        return int(self.lib.q4o_threads())
 
     # -- scalar conversions -------------------------------------------------
     def f32_to_f16_bits(self, f: float) -> int:

@@ -30,6 +30,9 @@
 
 #include <float.h>
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -205,4 +208,13 @@ int q4o_matmul(const uint16_t* x, const uint8_t* packed,
     }
     free(xd);
     return Q4O_OK;
+}
+
+/* Number of threads the parallel loops above use (1 without OpenMP). */
+int q4o_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -30,4 +30,7 @@ int q4o_matmul(const uint16_t* x, const uint8_t* packed,
                const uint16_t* scales, int64_t m, int64_t n, int64_t k,
                double* y, double* bound);
 
+/* Threads used by the parallel loops. */
+int q4o_threads(void);
+
 #endif

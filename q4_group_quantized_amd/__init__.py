@@ -1,0 +1,142 @@
+"""Python binding of the gfx950 Q4 library (``libq4.so``, C ABI in include/q4.h).
+
+Argument marshalling only: every step of quantization and of the product runs
+in the library's HIP kernels.  PyTorch provides device memory and the current
+stream.  There is no fallback: if ``libq4.so`` has not been built, or the
+current device is not a gfx950, calls raise.
+
+Functions keep the C names:
+  q4_quantize(w)                       -> (packed uint8 [n,k/2], scales fp16 [n,k/32])
+  q4_gemv(x, packed, scales)           -> y fp32 [m,n]     (1 <= m <= 8)
+  q4_gemm(x, packed, scales)           -> y fp32 [m,n]     (any m >= 1)
+  q4_status_str(code), q4_abi_version()
+Outputs may be passed in (``out=``) to avoid allocation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq4.so")
+
+EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm")
+Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE = range(6)
+GROUP = 32
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (status %d)" % (fn, q4_status_str(status), status))
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libq4.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libq4.so not built (%s); run python -m q4_group_quantized_amd.build"
+                          % path)
+    lib = ctypes.CDLL(path)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.q4_abi_version.argtypes = []
+    lib.q4_abi_version.restype = ctypes.c_int
+    lib.q4_status_str.argtypes = [ctypes.c_int]
+    lib.q4_status_str.restype = ctypes.c_char_p
+    lib.q4_quantize.argtypes = [p, p, p, i64, i64, p]
+    lib.q4_quantize.restype = ctypes.c_int
+    for name in ("q4_gemv", "q4_gemm"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, p, p, i64, i64, i64, p]
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def q4_abi_version() -> int:
+    return int(load().q4_abi_version())
+
+
+def q4_status_str(status: int) -> str:
+    return load().q4_status_str(int(status)).decode()
+
+
+def _stream(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != Q4_OK:
+        raise Q4Error(fn, status)
+
+
+def _require(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def q4_quantize(w, out: Optional[Tuple] = None, stream=None):
+    """fp32 [n, k] device tensor -> (packed uint8 [n, k/2], scales fp16 [n, k/32])."""
+    import torch
+    _require(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [n, k]")
+    n, k = w.shape
+    if out is None:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((n, k // GROUP), dtype=torch.float16, device=w.device)
+    else:
+        packed, scales = out
+    with torch.cuda.device(w.device):
+        st = load().q4_quantize(w.data_ptr(), packed.data_ptr(), scales.data_ptr(), n, k,
+                                _stream(stream, w.device))
+    _check("q4_quantize", st)
+    return packed, scales
+
+
+def _product(name, x, packed, scales, out, stream):
+    import torch
+    _require(x, torch.float16, "x")
+    _require(packed, torch.uint8, "packed")
+    _require(scales, torch.float16, "scales")
+    if x.dim() != 2 or packed.dim() != 2 or scales.dim() != 2:
+        raise ValueError("x, packed and scales must be 2-D")
+    m, k = x.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 2 != k or tuple(scales.shape) != (n, k // GROUP):
+        raise ValueError("shapes disagree: x %s packed %s scales %s"
+                         % (tuple(x.shape), tuple(packed.shape), tuple(scales.shape)))
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+    if out is not None:
+        _require(y, torch.float32, "out")
+        if tuple(y.shape) != (m, n):
+            raise ValueError("out must be [m, n]")
+    with torch.cuda.device(x.device):
+        st = getattr(load(), name)(x.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                                   y.data_ptr(), m, n, k, _stream(stream, x.device))
+    _check(name, st)
+    return y
+
+
+def q4_gemv(x, packed, scales, out=None, stream=None):
+    """Decode product, 1 <= m <= 8: y[m, n] = x[m, k] . dequant(packed, scales)^T."""
+    return _product("q4_gemv", x, packed, scales, out, stream)
+
+
+def q4_gemm(x, packed, scales, out=None, stream=None):
+    """Prefill product for any m >= 1 (tuned for m >= 16)."""
+    return _product("q4_gemm", x, packed, scales, out, stream)

@@ -1,0 +1,65 @@
+// q4_device.hpp -- device-side building blocks shared by the gfx950 kernels.
+//
+// The 16-entry dequantization table (QORA-LLM-0.8B model card, "AVX-512 SIMD
+// Acceleration", Q4 GEMV row; QORA-4B article, quantization section) maps a
+// stored 4-bit code v to the level v - 8.  On gfx950 the table is not a memory
+// lookup: a code is spliced into the low mantissa bits of the binary16
+// constant 1024.0 (bit pattern 0x6400), which gives exactly 1024 + v, and one
+// packed fp16 subtraction of 1032 yields v - 8, exact, for two codes at once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+constexpr uint32_t kMagic1024x2 = 0x64006400u;   // two binary16 1024.0
+
+__device__ __forceinline__ half2_t as_half2(uint32_t u) {
+    return __builtin_bit_cast(half2_t, u);
+}
+__device__ __forceinline__ uint32_t as_u32(half2_t h) {
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Eight codes of one packed dword -> eight exact fp16 levels.
+// Dword bits: code of element e (0..7) sits at bits 4e..4e+3.
+// Output order (lo half, hi half) per register: (e0,e4) (e1,e5) (e2,e6) (e3,e7),
+// i.e. the fp16 at position v of the 8-vector is element kUnpackOrder[v].
+__device__ __forceinline__ half8_t unpack8(uint32_t d) {
+    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    half2_t h0 = as_half2((d & kNibblePairMask) | kMagic1024x2) + bias;
+    half2_t h1 = as_half2(((d >> 4) & kNibblePairMask) | kMagic1024x2) + bias;
+    half2_t h2 = as_half2(((d >> 8) & kNibblePairMask) | kMagic1024x2) + bias;
+    half2_t h3 = as_half2(((d >> 12) & kNibblePairMask) | kMagic1024x2) + bias;
+    half8_t r;
+    r[0] = h0[0]; r[1] = h0[1];
+    r[2] = h1[0]; r[3] = h1[1];
+    r[4] = h2[0]; r[5] = h2[1];
+    r[6] = h3[0]; r[7] = h3[1];
+    return r;
+}
+
+// Eight consecutive fp16 activations (as four dwords x0x1, x2x3, x4x5, x6x7)
+// reordered to match unpack8: (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+__device__ __forceinline__ u32x4_t permute_x8(u32x4_t d) {
+    u32x4_t r;
+    r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+    r[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+    r[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+    return r;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+}  // namespace q4

@@ -1,0 +1,32 @@
+// q4_launch.hpp -- host launchers of the gfx950 kernels.  Arguments have
+// already been validated by the C ABI layer (q4_api.hip); each launcher only
+// picks a kernel configuration and enqueues it on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+struct DeviceInfo {
+    int cu_count;        // compute units of the current device
+};
+
+// Cached per-device facts (thread-safe, filled on first use of a device).
+const DeviceInfo& device_info(int device);
+
+// True when `device` (0 <= device < 64) is a gfx950 the kernels were built for.
+bool device_usable(int device);
+
+hipError_t launch_quantize(const float* w, uint8_t* packed, uint16_t* scales,
+                           int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed,
+                       const uint16_t* scales, float* y, int64_t m, int64_t n,
+                       int64_t k, hipStream_t stream);
+
+hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed,
+                       const uint16_t* scales, float* y, int64_t m, int64_t n,
+                       int64_t k, hipStream_t stream);
+
+}  // namespace q4

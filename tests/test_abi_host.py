@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI library (no GPU needed, nothing is launched).
+
+The library must load, export every entry point include/q4.h declares, and
+reject invalid arguments on the host before touching the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import q4_group_quantized_amd as q4
+    if not os.path.exists(q4.LIB_PATH):
+        from q4_group_quantized_amd import build
+        build.build()
+    return q4.load()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for fn in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_status_str", "q4_abi_version"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import q4_group_quantized_amd as q4
+    out = subprocess.run(["nm", "-D", "--defined-only", q4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (q4_[a-z_]+)\b", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    for f in declared_functions():
+        getattr(lib, f)
+
+
+def test_version_and_status_strings(lib):
+    m = re.search(r"#define Q4_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.q4_abi_version() == int(m.group(1))
+    seen = set()
+    for code in range(6):
+        s = lib.q4_status_str(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.q4_status_str(99).decode() == "unknown status"
+
+
+FAKE = 0x10000          # never dereferenced: validation fails before any use
+NULL = None
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, FAKE, FAKE, 4, 64), 1),
+    ((FAKE, NULL, FAKE, 4, 64), 1),
+    ((FAKE, FAKE, NULL, 4, 64), 1),
+    ((FAKE, FAKE, FAKE, 0, 64), 2),
+    ((FAKE, FAKE, FAKE, 4, 16), 2),
+    ((FAKE, FAKE, FAKE, 4, 48), 2),
+    ((FAKE, FAKE, FAKE, 2 ** 31, 64), 2),
+    ((FAKE, FAKE, FAKE, 4, 2 ** 24 + 32), 2),
+    ((FAKE, FAKE, FAKE, 2 ** 20, 2 ** 21), 2),
+    ((FAKE + 4, FAKE, FAKE, 4, 64), 3),
+    ((FAKE, FAKE + 8, FAKE, 4, 64), 3),
+    ((FAKE, FAKE, FAKE + 1, 4, 64), 3),
+])
+def test_quantize_rejects_bad_arguments(lib, args, expect):
+    assert lib.q4_quantize(*args, None) == expect
+
+
+@pytest.mark.parametrize("fn", ["q4_gemv", "q4_gemm"])
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, FAKE, FAKE, FAKE, 1, 8, 64), 1),
+    ((FAKE, NULL, FAKE, FAKE, 1, 8, 64), 1),
+    ((FAKE, FAKE, NULL, FAKE, 1, 8, 64), 1),
+    ((FAKE, FAKE, FAKE, NULL, 1, 8, 64), 1),
+    ((FAKE, FAKE, FAKE, FAKE, 0, 8, 64), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 0, 64), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 33), 2),
+    ((FAKE, FAKE, FAKE, FAKE, -3, 8, 64), 2),
+    ((FAKE + 2, FAKE, FAKE, FAKE, 1, 8, 64), 3),
+    ((FAKE, FAKE + 4, FAKE, FAKE, 1, 8, 64), 3),
+    ((FAKE, FAKE, FAKE + 1, FAKE, 1, 8, 64), 3),
+    ((FAKE, FAKE, FAKE, FAKE + 2, 1, 8, 64), 3),
+])
+def test_products_reject_bad_arguments(lib, fn, args, expect):
+    assert getattr(lib, fn)(*args, None) == expect
+
+
+def test_gemv_rejects_more_than_eight_rows(lib):
+    assert lib.q4_gemv(FAKE, FAKE, FAKE, FAKE, 9, 8, 64, None) == 2
+
+
+def test_binding_names_match_the_c_abi():
+    import q4_group_quantized_amd as q4
+    for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_status_str", "q4_abi_version"):
+        assert callable(getattr(q4, name))

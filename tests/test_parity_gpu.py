@@ -1,0 +1,237 @@
+"""GPU parity: the gfx950 library (through its C ABI) against the CPU oracle.
+
+Bars:
+  q4_quantize        bit-exact packed codes and fp16 scales
+  q4_gemv / q4_gemm  |y - y_ref| <= 1e-3 * sum|x*s*q| + 1e-6 for every output,
+                     exact where the result is exactly representable (one-hot x,
+                     x = 0, W = 0)
+Small cases span several tiles plus ragged tails and are compared in full;
+the five workload configurations run at full size and are compared on
+sampled rows (all m) that the oracle recomputes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+import q4_inputs as qi
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print("[parity] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import q4_group_quantized_amd as mod
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    mod.load()
+    return mod
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+DEV = "cuda:0"
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def gpu_quantize(q4, w):
+    packed, scales = q4.q4_quantize(gpu(w))
+    torch.cuda.synchronize()
+    return packed.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+
+
+def product(q4, fn, x, packed, scales):
+    y = getattr(q4, fn)(gpu(x), gpu(packed), gpu(scales.view(np.float16)))
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def assert_within(y, y_ref, bound, what):
+    err = np.abs(y - y_ref)
+    tol = oracle.tolerance(bound)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%s: %d outputs outside tolerance, first %s: y=%r ref=%r tol=%r" % (
+        what, len(bad), tuple(bad[0]), y[tuple(bad[0])], y_ref[tuple(bad[0])], tol[tuple(bad[0])])
+
+
+# --------------------------------------------------------------------------
+# quantizer
+# --------------------------------------------------------------------------
+
+def test_quantize_golden_groups(q4, orc):
+    golden = oracle_pins.load_golden()
+    w = np.stack([g["w"] for g in golden.values()])           # one group per row
+    _log("quantize golden groups %s" % (w.shape,))
+    packed, scales = gpu_quantize(q4, w)
+    for i, g in enumerate(golden.values()):
+        assert int(scales[i, 0]) == g["scale"]
+        assert np.array_equal(packed[i], g["bytes"])
+    wrow = w.reshape(1, -1)                                    # the same groups in one row
+    packed, scales = gpu_quantize(q4, wrow)
+    rp, rs = orc.quantize(wrow)
+    assert np.array_equal(packed, rp) and np.array_equal(scales, rs)
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (3, 96), (17, 160), (64, 2560), (1000, 1024),
+                                 (33, 32 * 37), (5, 65536)])
+def test_quantize_bit_exact(q4, orc, n, k):
+    rng = np.random.default_rng(n * 7919 + k)
+    w = oracle_pins.spread_weights(rng, n, k)
+    if k >= 64:
+        w[0, :32 * min(8, k // 32)] = oracle_pins._tie_groups(rng, min(8, k // 32)).reshape(-1)
+    w[-1, :32] = 0.0
+    _log("quantize n=%d k=%d" % (n, k))
+    packed, scales = gpu_quantize(q4, w)
+    rp, rs = orc.quantize(w)
+    assert np.array_equal(scales, rs), np.argwhere(scales != rs)[:5]
+    assert np.array_equal(packed, rp), np.argwhere(packed != rp)[:5]
+
+
+# --------------------------------------------------------------------------
+# products on small shapes, compared in full
+# --------------------------------------------------------------------------
+
+SHAPES = [(1, 32), (15, 64), (17, 96), (33, 256), (100, 1056), (257, 2560), (1024, 1024)]
+
+
+def _case(orc, m, n, k, seed):
+    rng = np.random.default_rng(seed)
+    w = oracle_pins.spread_weights(rng, n, k) if seed % 2 else \
+        (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = (rng.standard_normal((m, k)) * 2).astype(np.float16)
+    packed, scales = orc.quantize(w)
+    y_ref, bound = orc.matmul(x, packed, scales)
+    return x, packed, scales, y_ref, bound
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("fn", ["q4_gemv", "q4_gemm"])
+def test_decode_product(q4, orc, fn, m, n, k):
+    x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m * 1000 + n + k)
+    _log("%s m=%d n=%d k=%d" % (fn, m, n, k))
+    y = product(q4, fn, x, packed, scales)
+    assert_within(y, y_ref, bound, "%s m=%d n=%d k=%d" % (fn, m, n, k))
+
+
+@pytest.mark.parametrize("m", [9, 15, 16, 17, 31, 64, 100, 128, 129, 300])
+@pytest.mark.parametrize("n,k", [(17, 96), (64, 256), (130, 2560), (200, 160), (70, 1056)])
+def test_prefill_product(q4, orc, m, n, k):
+    x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m * 31 + n * 7 + k)
+    _log("q4_gemm m=%d n=%d k=%d" % (m, n, k))
+    y = product(q4, "q4_gemm", x, packed, scales)
+    assert_within(y, y_ref, bound, "q4_gemm m=%d n=%d k=%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("fn,m,k", [("q4_gemv", 1, 65536), ("q4_gemv", 8, 65536),
+                                    ("q4_gemm", 40, 65536), ("q4_gemv", 1, 2 ** 20)])
+def test_long_k(q4, orc, fn, m, k):
+    """K beyond what one LDS pass of activations holds."""
+    x, packed, scales, y_ref, bound = _case(orc, m, 3, k, seed=k + m)
+    _log("%s m=%d n=3 k=%d" % (fn, m, k))
+    y = product(q4, fn, x, packed, scales)
+    assert_within(y, y_ref, bound, "%s long k" % fn)
+
+
+@pytest.mark.parametrize("fn", ["q4_gemv", "q4_gemm"])
+def test_exact_special_inputs(q4, orc, fn):
+    rng = np.random.default_rng(77)
+    n, k = 37, 96
+    w = oracle_pins.spread_weights(rng, n, k)
+    packed, scales = orc.quantize(w)
+    q = oracle_pins.unpack_levels(packed).astype(np.float64)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 32, axis=1)
+    _log("%s one-hot / zero inputs" % fn)
+    step = 8 if fn == "q4_gemv" else k
+    for e0 in range(0, k, step):
+        x = np.eye(k, dtype=np.float16)[e0:e0 + step]
+        y = product(q4, fn, x, packed, scales)
+        assert np.array_equal(y, (s * q).T[e0:e0 + step]), "one-hot rows %d.." % e0
+    y = product(q4, fn, np.zeros((3, k), np.float16), packed, scales)
+    assert np.all(y == 0)
+    zp, zs = orc.quantize(np.zeros((n, k), np.float32))
+    y = product(q4, fn, rng.standard_normal((3, k)).astype(np.float16), zp, zs)
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("fn,m", [("q4_gemv", 1), ("q4_gemv", 8), ("q4_gemm", 200)])
+def test_deterministic(q4, orc, fn, m):
+    x, packed, scales, _, _ = _case(orc, m, 999, 2560, seed=5)
+    _log("%s determinism m=%d" % (fn, m))
+    a = product(q4, fn, x, packed, scales)
+    b = product(q4, fn, x, packed, scales)
+    assert np.array_equal(a, b)
+
+
+def test_non_default_stream(q4, orc):
+    x, packed, scales, y_ref, bound = _case(orc, 4, 300, 1024, seed=3)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xg, pg, sg = gpu(x), gpu(packed), gpu(scales.view(np.float16))
+        y = q4.q4_gemv(xg, pg, sg)
+    s.synchronize()
+    assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound, "stream")
+
+
+def test_binding_rejects_bad_calls(q4):
+    x = torch.zeros((9, 64), dtype=torch.float16, device=DEV)
+    p = torch.zeros((4, 32), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((4, 2), dtype=torch.float16, device=DEV)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv(x, p, s)
+    with pytest.raises(ValueError):
+        q4.q4_gemm(x, p[:, :16], s)
+
+
+# --------------------------------------------------------------------------
+# the five workload configurations at full size, compared on sampled rows
+# --------------------------------------------------------------------------
+
+def _sample_rows(n, rng, count=384):
+    if n <= count:
+        return np.arange(n)
+    pick = rng.choice(n, count - 64, replace=False)
+    return np.unique(np.concatenate([np.arange(32), np.arange(n - 32, n), pick]))
+
+
+CASES = [(wl.key, i) for wl in qi.WORKLOADS.values() for i in range(len(wl.cases))]
+
+
+@pytest.mark.parametrize("key,idx", CASES, ids=["%s-%d" % c for c in CASES])
+def test_workload_full_size(q4, orc, key, idx):
+    wl = qi.WORKLOADS[key]
+    mat, m = wl.cases[idx]
+    fn = "q4_gemv" if m <= 8 else "q4_gemm"
+    _log("%s %s m=%d n=%d k=%d: generating" % (key, mat.name, m, mat.n, mat.k))
+    w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id, wide_groups=mat.wide_groups)
+    x = qi.activations(m, mat.k, outliers=wl.outliers)
+    wg = gpu(w)
+    packed, scales = q4.q4_quantize(wg)
+    del wg
+    _log("%s: %s" % (mat.name, fn))
+    y = getattr(q4, fn)(gpu(x), packed, scales)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(mat.tensor_id)
+    rows = _sample_rows(mat.n, rng)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    gp = packed.index_select(0, rows_t).cpu().numpy()
+    gs = scales.index_select(0, rows_t).cpu().numpy().view(np.uint16)
+    gy = y.index_select(1, rows_t).cpu().numpy().astype(np.float64)
+    # the oracle quantizes the same generated rows itself
+    rp, rs = orc.quantize(w[rows])
+    assert np.array_equal(gs, rs) and np.array_equal(gp, rp), "quantize mismatch"
+    y_ref, bound = orc.matmul(x, rp, rs)
+    assert_within(gy, y_ref, bound, "%s %s" % (key, mat.name))
