@@ -66,17 +66,25 @@ def kernel_source_hash() -> str:
 # --------------------------------------------------------------------------
 
 def rocprof_summary(path: str) -> None:
-    import csv
+    """Average kernel durations by (kernel, grid size) from a rocprofv3 kernel
+    trace: either a *_kernel_trace.csv or a rocpd *_results.db."""
     groups = {}
-    with open(path) as fh:
-        for row in csv.DictReader(fh):
-            name = row.get("Kernel_Name", "?")
-            grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "?"
-            dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
-            groups.setdefault((name, grid), []).append(dur)
-    print("%-10s %-8s %-12s %-12s %s" % ("grid", "calls", "avg_ns", "min_ns", "kernel"))
+    if path.endswith(".db"):
+        import sqlite3
+        con = sqlite3.connect(path)
+        for name, grid, dur in con.execute("select name, grid_x, end - start from kernels"):
+            groups.setdefault((name, str(grid)), []).append(int(dur))
+    else:
+        import csv
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name", "?")
+                grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "?"
+                dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+                groups.setdefault((name, grid), []).append(dur)
+    print("%-10s %-8s %-12s %-12s %s" % ("grid_x", "calls", "avg_ns", "min_ns", "kernel"))
     for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        short = name if len(name) < 90 else name[:87] + "..."
+        short = name if len(name) < 100 else name[:97] + "..."
         print("%-10s %-8d %-12.0f %-12d %s" % (grid, len(d), sum(d) / len(d), min(d), short))
 
 
@@ -243,36 +251,35 @@ def quantize_rate(torch, q4, mat, iters):
 # CPU baseline: the oracle on a bounded sample of the decode set
 # --------------------------------------------------------------------------
 
-def cpu_baseline(workload, budget_s=12.0):
+def cpu_baseline(workload, budget_s=10.0):
+    """Oracle product over the whole decode set, repeated for ~budget_s."""
     import oracle
     import q4_inputs as qi
     o = oracle.get()
     mats = [mat for mat, _ in workload.cases]
-    k = mats[0].k
-    x = qi.activations(1, k, outliers=workload.outliers)
-    total_t, total_b, parts = 0.0, 0, []
+    x = qi.activations(1, mats[0].k, outliers=workload.outliers)
+    quantized = []
+    t0 = time.perf_counter()
     for mat in mats:
-        rows = mat.n
-        if mat.n > 8192:
-            # calibrate on 2048 rows, then size the sample to the remaining budget
-            w = qi.weight_rows(mat.n, mat.k, 0, 2048, tensor_id=mat.tensor_id)
-            p, s = o.quantize(w)
-            t0 = time.perf_counter()
+        w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id, wide_groups=mat.wide_groups)
+        tq = time.perf_counter()
+        quantized.append(o.quantize(w))
+        t0 += time.perf_counter() - tq     # generation time is not oracle work
+    set_bytes = sum(qi.workload_bytes(1, mat.n, mat.k) for mat in mats)
+    times = []
+    start = time.perf_counter()
+    while not times or (time.perf_counter() - start < budget_s and len(times) < 1000):
+        t = time.perf_counter()
+        for p, s in quantized:
             o.matmul(x, p, s)
-            dt = time.perf_counter() - t0
-            rows = int(min(mat.n, max(2048, 2048 * max(budget_s - total_t, 1.0) / max(dt, 1e-6))))
-        w = qi.weight_rows(mat.n, mat.k, 0, rows, tensor_id=mat.tensor_id)
-        p, s = o.quantize(w)
-        t0 = time.perf_counter()
-        o.matmul(x, p, s)
-        dt = time.perf_counter() - t0
-        total_t += dt
-        total_b += qi.workload_bytes(1, rows, mat.k)
-        parts.append("%s %d/%d rows" % (mat.name, rows, mat.n))
-    return {"value": round(total_b / total_t / 1e9, 3), "unit": "GB/s", "cores": o.threads(),
+        times.append(time.perf_counter() - t)
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": round(set_bytes / med / 1e9, 3), "unit": "GB/s", "cores": o.threads(),
             "kind": "oracle",
-            "sample": "oracle q4o_matmul (fp64) on the decode set at M=1: " + ", ".join(parts)
-                      + "; %.1f s of CPU time" % total_t}
+            "sample": ("whole 0.8B decode set at M=1 (7 matrices, %.1f MB algorithmic), oracle "
+                       "q4o_matmul in fp64, median of %d passes (%.1f s)"
+                       % (set_bytes / 1e6, len(times), sum(times)))}
 
 
 # --------------------------------------------------------------------------
@@ -284,7 +291,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--all", action="store_true", help="also time the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rocprof-summary", metavar="KERNEL_TRACE_CSV")
+    ap.add_argument("--rocprof-summary", metavar="TRACE_CSV_OR_DB")
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
@@ -292,7 +299,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this Q4 GEMV/GEMM path runs on one GPU; --gpus %d is not supported "
-              "(sharding is described in DESIGN.md, not built)" % max(args.gpus, world),
+              "(single-GPU build)" % max(args.gpus, world),
               file=sys.stderr)
         return 2
 

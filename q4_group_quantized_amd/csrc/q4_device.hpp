@@ -58,6 +58,82 @@ __device__ __forceinline__ u32x4_t permute_x8(u32x4_t d) {
     return r;
 }
 
+// Constants of the nibble splice, passed to the kernels as an argument.
+// gfx9 VOP3 encodings cannot carry two literal constants, so with literals
+// the compiler splits (d & mask) | magic into two instructions; values the
+// optimizer cannot see are kept in registers and give one v_and_or_b32.
+// (No inline asm anywhere: it would make the compiler reserve AGPRs and route
+// every MFMA result through them.)
+struct SpliceConsts {
+    uint32_t mask;       // kNibblePairMask
+    uint32_t magic;      // kMagic1024x2
+    uint32_t sel[4];     // byte selectors of unpack8_natural
+};
+constexpr SpliceConsts kSpliceConsts = {kNibblePairMask, kMagic1024x2,
+                                        {0x0C040C00u, 0x0C050C01u, 0x0C060C02u, 0x0C070C03u}};
+
+// A kernel-argument value copied into a VGPR (identity DPP move): with the
+// mask in an SGPR and the magic in a VGPR the splice is one v_and_or_b32
+// (one scalar operand per VOP3).
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, false);
+}
+
+// The same table lookup as unpack8, returned as four fp16 pairs
+// (e0,e4) (e1,e5) (e2,e6) (e3,e7) for v_dot2_f32_f16.  mask and magic are
+// kNibblePairMask and kMagic1024x2 held in registers by the caller.
+__device__ __forceinline__ void unpack8_pairs(uint32_t d, uint32_t mask, uint32_t magic,
+                                              half2_t (&h)[4]) {
+    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    h[0] = as_half2((d & mask) | magic) + bias;
+    h[1] = as_half2(((d >> 4) & mask) | magic) + bias;
+    h[2] = as_half2(((d >> 8) & mask) | magic) + bias;
+    h[3] = as_half2(((d >> 12) & mask) | magic) + bias;
+}
+
+// The table lookup in natural element order, for operands whose activations
+// are used as stored: output fp16 v = level of element v (v = 0..7).
+// sel[i] = 0x0C040C00 + i * 0x00010001 picks byte i of d into the low half
+// and byte i of d >> 4 into the high half; the mask keeps one code per half.
+__device__ __forceinline__ half8_t unpack8_natural(uint32_t d, uint32_t mask, uint32_t magic,
+                                                   const uint32_t (&sel)[4]) {
+    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const uint32_t u = d >> 4;
+    half8_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2_t h = as_half2((__builtin_amdgcn_perm(u, d, sel[i]) & mask) | magic) + bias;
+        r[2 * i] = h[0];
+        r[2 * i + 1] = h[1];
+    }
+    return r;
+}
+
+// Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15); every lane of
+// the row receives the total.  Rotations by 8, 4, 2, 1 within the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+    return v;
+}
+
+// Workgroup barrier that leaves outstanding global loads in flight
+// (__syncthreads() also fences memory, which drains every pending load).
+// The signal fences only stop the compiler from moving memory accesses across
+// it.  Callers first wait themselves for the data other waves will read:
+// vmcnt for direct-to-LDS loads, lgkmcnt for LDS stores.
+__device__ __forceinline__ void barrier_keep_loads() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

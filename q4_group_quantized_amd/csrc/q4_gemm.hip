@@ -6,213 +6,273 @@
 // format of their quantization sections (symmetric, group size 32, 16-entry
 // table dequantization).
 //
-// Tiling.  A workgroup owns a BM x BN tile of y and walks K two groups (64
-// elements) per stage.  Each stage stages through LDS, double-buffered:
-//   - the BM x 64 activation tile, permuted inside every 8-element chunk to
-//     the order in which unpack8 emits codes;
-//   - the BN x 32 packed-code tile (raw nibbles, 0.5 byte per weight);
-//   - the BN x 2 fp16 scales.
-// Global loads of stage s+1 are issued before the MFMAs of stage s.
+// Arithmetic.  For every 32-element group j, one v_mfma_f32_16x16x32_f16 per
+// 16x16 output block multiplies fp16 activations by the group's exact fp16
+// levels -8..7 (K = 32 is exactly one group) into a fresh accumulator P, and
+// the group's scale is applied in fp32 afterwards: acc += s[n, j] * P.  In the
+// 16x16 D layout a lane's four values share one column, hence one scale.
 //
-// Per group, each wave turns one packed dword per lane into eight exact fp16
-// levels -8..7 (the table lookup, see q4_device.hpp), runs one
-// v_mfma_f32_16x16x32_f16 per 16x16 block with a zero accumulator -- K = 32 is
-// exactly one group -- and folds the result into its fp32 accumulators with
-// the group's scale: acc += s[n, j] * P.  In the 16x16 D layout a lane's four
-// values share one column, hence one scale.
+// Work split.  A workgroup (4 or 8 waves: one or two per SIMD) owns a
+// BM x (32*WN) tile of y.  Its waves are WN column slices of 32 x WK slices of K: each wave covers
+// all BM rows and 32 columns over G/WK groups, so every code is unpacked by
+// exactly one wave and every activation is read from LDS by WN waves.  The
+// WK partial tiles are added in LDS at the end in a fixed order
+// (deterministic).
+//
+// Data movement.  Every operand goes straight from global memory into LDS
+// with direct-to-LDS loads, through an S-stage ring per K slice:
+//   activations  16 rows x 64 bytes of one group per wave instruction (1 KiB);
+//                each lane reads its A operand with one ds_read_b128
+//   codes        one whole 16-byte group of 64 columns per instruction
+//   scales       one fp16 per column, each landing in a 4-byte LDS slot
+// so the loop body issues no register-destination global loads and the only
+// waits on global memory are the explicit per-stage vmcnt waits below.
+// Rows past M, columns past N and groups past G are clamped to real
+// addresses: their results are never stored, and out-of-range groups are
+// never computed.
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
 
 namespace q4 {
 namespace {
 
-constexpr int kKG = 2;                               // groups per stage
-constexpr int kXRow = kKG * 32 + 8;                  // halves per LDS row (padded)
-constexpr int kWRow = kKG * 16 + 4;                  // bytes per LDS row (padded)
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int BM, int BN, int WM, int WN>
-struct GemmCfg {
-    static constexpr int kThreads = 64 * WM * WN;
-    static constexpr int TM = BM / WM;               // wave tile
-    static constexpr int TN = BN / WN;
-    static constexpr int MB = TM / 16;               // MFMA blocks per wave
-    static constexpr int NB = TN / 16;
-    static constexpr int kXUnits = BM * kKG * 4;     // 16-byte units per stage
-    static constexpr int kWUnits = BN * kKG;
-    static constexpr int kSUnits = BN * kKG;
-    static constexpr int kXPer = (kXUnits + kThreads - 1) / kThreads;
-    static constexpr int kWPer = (kWUnits + kThreads - 1) / kThreads;
-    static constexpr int kSPer = (kSUnits + kThreads - 1) / kThreads;
-    static_assert(MB >= 1 && NB >= 1, "wave tile below one MFMA block");
-};
+constexpr int kBlockBytes = 1024;          // one (group, 16-row block) of activations
 
-template <class C>
-struct StageRegs {
-    u32x4_t xv[C::kXPer];
-    u32x4_t wv[C::kWPer];
-    uint32_t sv[C::kSPer];
-};
-
-template <int BM, int BN, class C>
-__device__ __forceinline__ void load_stage(StageRegs<C>& r, const uint16_t* __restrict__ x,
-                                           const uint8_t* __restrict__ packed,
-                                           const uint16_t* __restrict__ scales,
-                                           int64_t m0, int64_t n0, int M, int64_t N,
-                                           int K, int G, int j0) {
-#pragma unroll
-    for (int i = 0; i < C::kXPer; ++i) {
-        const int u = threadIdx.x + i * C::kThreads;
-        r.xv[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (u < C::kXUnits) {
-            const int row = u / (kKG * 4);
-            const int rest = u % (kKG * 4);
-            const int j = j0 + rest / 4;
-            const int64_t m = m0 + row;
-            if (m < M && j < G)
-                r.xv[i] = *reinterpret_cast<const u32x4_t*>(x + m * K + 32 * j + 8 * (rest & 3));
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::kWPer; ++i) {
-        const int u = threadIdx.x + i * C::kThreads;
-        r.wv[i] = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-        if (u < C::kWUnits) {
-            const int row = u / kKG;
-            const int j = j0 + u % kKG;
-            const int64_t n = n0 + row;
-            if (n < N && j < G)
-                r.wv[i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t*>(packed + n * (K / 2) + 16 * j));
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::kSPer; ++i) {
-        const int u = threadIdx.x + i * C::kThreads;
-        r.sv[i] = 0u;
-        if (u < C::kSUnits) {
-            const int row = u / kKG;
-            const int j = j0 + u % kKG;
-            const int64_t n = n0 + row;
-            if (n < N && j < G) r.sv[i] = scales[n * G + j];
-        }
-    }
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+    // s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 (gfx9)
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-template <int BM, int BN, class C>
-__device__ __forceinline__ void store_stage(const StageRegs<C>& r, _Float16* xs, uint8_t* ws,
-                                            uint16_t* ss) {
-#pragma unroll
-    for (int i = 0; i < C::kXPer; ++i) {
-        const int u = threadIdx.x + i * C::kThreads;
-        if (u < C::kXUnits) {
-            const int row = u / (kKG * 4);
-            const int rest = u % (kKG * 4);
-            *reinterpret_cast<u32x4_t*>(xs + row * kXRow + 8 * rest) = permute_x8(r.xv[i]);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::kWPer; ++i) {
-        const int u = threadIdx.x + i * C::kThreads;
-        if (u < C::kWUnits) {
-            const int row = u / kKG;
-            uint32_t* dst = reinterpret_cast<uint32_t*>(ws + row * kWRow + 16 * (u % kKG));
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dst[q] = r.wv[i][q];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::kSPer; ++i) {
-        const int u = threadIdx.x + i * C::kThreads;
-        if (u < C::kSUnits) ss[(u % kKG) * BN + u / kKG] = (uint16_t)r.sv[i];
-    }
-}
+template <int BM, int WN, int WK, int KG, int S>
+struct Gemm {
+    static constexpr int MB = BM / 16;                     // 16-row blocks per wave
+    static constexpr int BN = 32 * WN;
+    static constexpr int kCodeOff = KG * MB * kBlockBytes;           // within a stage
+    static constexpr int kScaleOff = kCodeOff + KG * kBlockBytes;
+    static constexpr int kStageBytes = kScaleOff + KG * 256;         // per K slice
+    static constexpr int kABlocksPerWave = KG * MB / WN;
+    // codes + scales of group gl are loaded by wave gl % WN of the K slice
+    static constexpr int groups_of(int wn) { return (KG - wn + WN - 1) / WN; }
+    static constexpr int loads_per_stage(int wn) { return kABlocksPerWave + 2 * groups_of(wn); }
+    static constexpr int kLdsBytes = WK * S * kStageBytes;
+    static constexpr int kRedBytes = (WK - 1) * WN * MB * 8 * 64 * 4;
+    static constexpr int kThreads = 64 * WN * WK;
+    static_assert(WN * WK == 4 || WN * WK == 8, "one or two waves per SIMD");
+    static_assert((KG * MB) % WN == 0, "activation blocks split evenly");
+    static_assert(S >= 2, "at least double buffering");
+    static_assert(kRedBytes <= kLdsBytes, "reduction fits in the staging space");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+};
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
+// At least two waves per SIMD: caps a wave at 256 registers, which also makes
+// the compiler keep MFMA results in VGPRs instead of routing them through
+// AGPRs (four v_accvgpr_read per 16x16 block before the scale FMAs).
+template <int BM, int WN, int WK, int KG, int S>
+__global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, float* __restrict__ y, int M, int64_t N,
-    int K, int G) {
-    using C = GemmCfg<BM, BN, WM, WN>;
-    __shared__ __align__(16) _Float16 xs[2][BM * kXRow];
-    __shared__ __align__(16) uint8_t ws[2][BN * kWRow];
-    __shared__ __align__(16) uint16_t ss[2][kKG * BN];
+    const uint16_t* __restrict__ scales, float* __restrict__ y, int M, int64_t N, int K,
+    int G, int64_t tiles_n, SpliceConsts kc) {
+    using C = Gemm<BM, WN, WK, KG, S>;
+    constexpr int MB = C::MB;
+    extern __shared__ __align__(16) unsigned char smem[];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int64_t tiles_n = (N + BN - 1) / BN;
-    const int64_t n0 = ((int64_t)blockIdx.x % tiles_n) * BN;
+    const int wn = wave % WN;
+    const int kp = wave / WN;
+    const int64_t nt0 = ((int64_t)blockIdx.x % tiles_n) * C::BN;     // tile's first column
     const int64_t m0 = ((int64_t)blockIdx.x / tiles_n) * BM;
+
+    const int Gp = (G + WK - 1) / WK;                     // groups per K slice
+    const int gbeg = kp * Gp;
+    const int gend = min(G, gbeg + Gp);
+    const int nstages = (Gp + KG - 1) / KG;               // same for every wave
+
+    unsigned char* kbase = smem + (size_t)kp * S * C::kStageBytes;
+    // Workgroups start their walk over K at different stages so that the CUs
+    // sharing an L2 do not all request the same activation columns at once.
+    // The order of the fp32 sums changes with it, identically on every run.
+    const int rot = (int)(blockIdx.x % (uint32_t)nstages);
+    auto stage_group = [&](int st) {               // first group (in the slice) of stage st
+        const int r = st + rot;
+        return (r < nstages ? r : r - nstages) * KG;
+    };
+
+    // load-side lane mappings
+    const int a_row = lane >> 2, a_part = lane & 3;       // 16 rows x 4 16-byte parts
+    const int64_t ld_col = min<int64_t>(nt0 + lane, N - 1);   // codes / scales: lane = column
+    const uint8_t* code_row = packed + ld_col * (K / 2);
+    const uint16_t* scale_row = scales + ld_col * G;
+    // operand-side lane mapping
     const int col = lane & 15, kq = lane >> 4;
 
-    float4_t acc[C::MB][C::NB];
+    auto issue = [&](int st, int buf) {
+        unsigned char* sb = kbase + buf * C::kStageBytes;
+        const int gs = gbeg + stage_group(st);
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i)
+        for (int i = 0; i < C::kABlocksPerWave; ++i) {
+            const int b = wn * C::kABlocksPerWave + i;
+            const int gl = b / MB, mb = b % MB;
+            const int g = min(gs + gl, G - 1);
+            const int64_t r = min<int64_t>(m0 + 16 * mb + a_row, M - 1);
+            __builtin_amdgcn_global_load_lds(x + r * K + 32 * g + 8 * a_part,
+                                             (lds_void_t*)(sb + (gl * MB + mb) * kBlockBytes),
+                                             16, 0, 0);
+        }
 #pragma unroll
-        for (int j = 0; j < C::NB; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int gl = 0; gl < KG; ++gl) {
+            if (gl % WN != wn) continue;
+            const int g = min(gs + gl, G - 1);
+            __builtin_amdgcn_global_load_lds(code_row + 16 * g,
+                                             (lds_void_t*)(sb + C::kCodeOff + gl * kBlockBytes),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(scale_row + g,
+                                             (lds_void_t*)(sb + C::kScaleOff + gl * 256), 2, 0,
+                                             0);
+        }
+    };
 
-    const int stages = (G + kKG - 1) / kKG;
-    StageRegs<C> regs;
-    load_stage<BM, BN, C>(regs, x, packed, scales, m0, n0, M, N, K, G, 0);
-    store_stage<BM, BN, C>(regs, xs[0], ws[0], ss[0]);
-    __syncthreads();
+    float4_t acc[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int s = 0; s < stages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < stages)
-            load_stage<BM, BN, C>(regs, x, packed, scales, m0, n0, M, N, K, G, (s + 1) * kKG);
+    const uint32_t mask = kc.mask;
+    const uint32_t magic = to_vgpr(kc.magic);
+    const uint32_t sel[4] = {kc.sel[0], kc.sel[1], kc.sel[2], kc.sel[3]};
+
 #pragma unroll
-        for (int g = 0; g < kKG; ++g) {
-            half8_t a[C::MB];
+    for (int u = 0; u < S - 1; ++u) issue(u, u);
+
+    // Operands of one group, read from LDS ahead of use: while a group's
+    // MFMAs and scale FMAs run, the next group's reads are in flight.
+    struct Ops {
+        half8_t a[MB];
+        uint32_t code[2];
+        _Float16 sc[2];
+    };
+    auto read_ops = [&](Ops& o, const unsigned char* sb, int gl) {
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb)
-                a[mb] = *reinterpret_cast<const half8_t*>(
-                    &xs[buf][(wm * C::TM + mb * 16 + col) * kXRow + g * 32 + 8 * kq]);
-            half8_t b[C::NB];
-            float sc[C::NB];
+        for (int mb = 0; mb < MB; ++mb)
+            o.a[mb] = *reinterpret_cast<const half8_t*>(sb + (gl * MB + mb) * kBlockBytes +
+                                                        64 * col + 16 * kq);
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
-                const int r = wn * C::TN + nb * 16 + col;
-                b[nb] = unpack8(*reinterpret_cast<const uint32_t*>(
-                    &ws[buf][r * kWRow + g * 16 + 4 * kq]));
-                sc[nb] = half_bits_to_float(ss[buf][g * BN + r]);
+        for (int nb = 0; nb < 2; ++nb) {
+            const int c = 32 * wn + 16 * nb + col;
+            o.code[nb] = *reinterpret_cast<const uint32_t*>(sb + C::kCodeOff + gl * kBlockBytes +
+                                                            16 * c + 4 * kq);
+            o.sc[nb] = *reinterpret_cast<const _Float16*>(sb + C::kScaleOff + gl * 256 + 4 * c);
+        }
+    };
+    auto compute = [&](const Ops& o) {
+        half8_t bh[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bh[nb] = unpack8_natural(o.code[nb], mask, magic, sel);
+        // all MFMAs of the group first, so their latencies overlap, then the
+        // scale FMAs
+        float4_t p[MB][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+                p[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a[mb], bh[nb], zero, 0, 0, 0);
             }
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb)
+        for (int nb = 0; nb < 2; ++nb) {
+            const float s = (float)o.sc[nb];
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) {
-                    const float4_t zero = {0.f, 0.f, 0.f, 0.f};
-                    float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], b[nb], zero, 0, 0, 0);
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(sc[nb], p[v], acc[mb][nb][v]);
-                }
+                for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(s, p[mb][nb][v], acc[mb][nb][v]);
         }
-        if (s + 1 < stages)
-            store_stage<BM, BN, C>(regs, xs[buf ^ 1], ws[buf ^ 1], ss[buf ^ 1]);
-        __syncthreads();
+    };
+
+    for (int st0 = 0; st0 < nstages; st0 += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int st = st0 + u;
+            if (st < nstages) {
+                // stage st has landed once at most the S-2 later stages remain in
+                // flight (wave-uniform branch: the count depends on the wave's share)
+                if (WN == 1 || wn == 0)
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(0) * (S - 2)));
+                else if (wn == 1)
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(1) * (S - 2)));
+                else
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(WN - 1) * (S - 2)));
+                barrier_keep_loads();
+                // refill the buffer computed last iteration (every wave is past it)
+                issue(st + S - 1, (u + S - 1) % S);
+                const unsigned char* sb = kbase + u * C::kStageBytes;
+                const int g0 = gbeg + stage_group(st);
+                Ops ops[2];
+                read_ops(ops[0], sb, 0);
+#pragma unroll
+                for (int gl = 0; gl < KG; ++gl) {
+                    if (gl + 1 < KG) read_ops(ops[(gl + 1) & 1], sb, gl + 1);
+                    if (g0 + gl < gend) compute(ops[gl & 1]);
+                }
+            }
+        }
     }
 
+    // add the K slices: slices 1..WK-1 park their partial tiles in LDS, slice
+    // 0 adds them in slice order and stores
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    if (kp > 0) {
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-            const int64_t n = n0 + wn * C::TN + nb * 16 + col;
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t m = m0 + wm * C::TM + mb * 16 + 4 * kq + v;
-                if (m < M && n < N) y[m * N + n] = acc[mb][nb][v];
+                for (int v = 0; v < 4; ++v)
+                    red[((((kp - 1) * WN + wn) * MB + mb) * 8 + nb * 4 + v) * 64 + lane] =
+                        acc[mb][nb][v];
+    }
+    __syncthreads();
+    if (kp == 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int64_t n = nt0 + 32 * wn + 16 * nb + col;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float t = acc[mb][nb][v];
+#pragma unroll
+                    for (int q = 1; q < WK; ++q)
+                        t += red[((((q - 1) * WN + wn) * MB + mb) * 8 + nb * 4 + v) * 64 + lane];
+                    const int64_t m = m0 + 16 * mb + 4 * kq + v;
+                    if (m < M && n < N) y[m * N + n] = t;
+                }
             }
-        }
+    }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int WN, int WK, int KG, int S>
 hipError_t launch_gemm_t(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
                          float* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-    const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
+    using C = Gemm<BM, WN, WK, KG, S>;
+    const int64_t tiles_n = (n + C::BN - 1) / C::BN;
+    const int64_t tiles = tiles_n * ((m + BM - 1) / BM);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN>), dim3((unsigned)tiles),
-                       dim3(64 * WM * WN), 0, stream, x, packed, scales, y, (int)m, n,
-                       (int)k, (int)(k / 32));
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&gemm_kernel<BM, WN, WK, KG, S>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
+                       dim3(C::kThreads), C::kLdsBytes, stream, x, packed, scales, y, (int)m, n,
+                       (int)k, (int)(k / 32), tiles_n, kSpliceConsts);
     return hipGetLastError();
 }
 
@@ -221,9 +281,10 @@ hipError_t launch_gemm_t(const uint16_t* x, const uint8_t* packed, const uint16_
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
                        float* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
     if (m <= 8) return launch_gemv(x, packed, scales, y, m, n, k, stream);
-    if (m <= 16) return launch_gemm_t<16, 64, 1, 4>(x, packed, scales, y, m, n, k, stream);
-    if (m < 128) return launch_gemm_t<64, 64, 2, 2>(x, packed, scales, y, m, n, k, stream);
-    return launch_gemm_t<128, 64, 2, 2>(x, packed, scales, y, m, n, k, stream);
+    if (m <= 16) return launch_gemm_t<16, 1, 4, 2, 4>(x, packed, scales, y, m, n, k, stream);
+    if (m <= 32) return launch_gemm_t<32, 1, 4, 2, 4>(x, packed, scales, y, m, n, k, stream);
+    if (m < 256) return launch_gemm_t<64, 2, 4, 2, 2>(x, packed, scales, y, m, n, k, stream);
+    return launch_gemm_t<128, 2, 4, 2, 2>(x, packed, scales, y, m, n, k, stream);
 }
 
 }  // namespace q4

@@ -127,6 +127,18 @@ def test_decode_product(q4, orc, fn, m, n, k):
     assert_within(y, y_ref, bound, "%s m=%d n=%d k=%d" % (fn, m, n, k))
 
 
+@pytest.mark.parametrize("k", [256, 512, 768, 1024, 1280, 1536, 1792, 2048, 2304, 2560, 3072,
+                               3584, 4096, 5120, 6144, 8192])
+@pytest.mark.parametrize("n", [1, 3, 5, 61, 4099])
+def test_single_token_streaming(q4, orc, n, k):
+    """m = 1 streaming kernel: every lanes-per-row / groups-per-lane variant,
+    ragged row counts (not a multiple of the rows per wave step)."""
+    x, packed, scales, y_ref, bound = _case(orc, 1, n, k, seed=n * 13 + k)
+    _log("q4_gemv m=1 n=%d k=%d" % (n, k))
+    y = product(q4, "q4_gemv", x, packed, scales)
+    assert_within(y, y_ref, bound, "q4_gemv m=1 n=%d k=%d" % (n, k))
+
+
 @pytest.mark.parametrize("m", [9, 15, 16, 17, 31, 64, 100, 128, 129, 300])
 @pytest.mark.parametrize("n,k", [(17, 96), (64, 256), (130, 2560), (200, 160), (70, 1056)])
 def test_prefill_product(q4, orc, m, n, k):
