@@ -6,27 +6,41 @@
 Prints ONE JSON line.  The workload is the 0.8B-shaped decode set at M = 1
 (hidden 1024: DeltaNet q/k/v 3 x 2048 rows, attention q 2048, k 512, v 512,
 LM head 248,320 rows), weights ~ N(0, 0.02^2) quantized on the GPU, x ~ N(0,1)
-in fp16.  One step is one decode pass: the seven q4_gemv products on the same
-x, replayed from a HIP graph.  The step rotates through enough copies of the
-quantized weights (>= 1 GiB) that no step finds its weights in the 256 MB
+in fp16.  One step is one decode pass over the seven matrices, launched as the
+model would group them by shared input: one q4_gemv_multi for the DeltaNet
+q/k/v projections, one for the attention q/k/v projections, and the LM head,
+replayed from a HIP graph (detail also times seven separate q4_gemv launches
+and one launch over all seven).  The step rotates through enough copies of
+the quantized weights (>= 1 GiB) that no step finds its weights in the 256 MB
 Infinity Cache: the figure is HBM-bound throughput, not cache bandwidth.
 
 value    = algorithmic bytes of one step / step time (GB/s); algorithmic bytes
            of one product = n*k/2 (codes) + n*k/16 (fp16 scales) + 2*m*k (x)
            + 4*m*n (y)
 roofline = the dominant kernel (the LM-head GEMV): its algorithmic bytes per
-           launch / its average launch duration from HIP events, against the
-           8 TB/s HBM3E peak
-detail   = the other halves of the hot path measured in the same run: the
-           M = 512 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s dense fp16
-           MFMA peak) and the quantizer (GB/s); --all adds the 4B decode set,
-           the M = 8 verify LM head and the M = 16/128/2048 prefill GEMMs
+           launch / its average launch duration (HIP events on the launching
+           stream around a batch of back-to-back launches over the rotated
+           copies), against the 8 TB/s HBM3E peak
+detail   = the other halves of the hot path measured in the same run: the 4B
+           LM head (k = 2560), the M = 512 prefill GEMM (TFLOP/s against the
+           2.5 PFLOP/s dense fp16 MFMA peak) and the quantizer (GB/s); --all
+           adds the 4B decode set, the M = 8 verify LM head and the
+           M = 16/128/2048 prefill GEMMs
 cpu_baseline = the CPU oracle (plain C, fp64 product) on a bounded sample of
            the same decode set, GB/s over the same algorithmic bytes
 
 --rocprof-summary TRACE.csv groups a rocprofv3 kernel trace by kernel and
 grid size (the LM head and the projections run the same kernel at different
 grid sizes) and prints average durations.
+
+--traffic-probe runs three launches of the 0.8B LM-head GEMV and three of a
+plain elementwise copy of known size (torch.neg over 256 MiB of fp32), for two
+`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` passes;
+--traffic-record FETCH.csv WRITE.csv turns their counter files into the HBM
+bytes per GEMV launch: each counter is scaled by the factor that maps the
+copy's reading onto the copy's known 256 MiB, and the result is stored with a
+hash of the kernel sources in profiles/gemv_lmhead_08b_traffic.txt, from where
+the roofline's `traffic` is read while the sources are unchanged.
 """
 from __future__ import annotations
 
@@ -44,7 +58,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFS = 2500.0    # MI355X dense fp16 MFMA
 ROTATE_BYTES = 1 << 30         # rotate through >= 1 GiB of weight copies
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lmhead_08b_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lmhead_08b_traffic.txt")
+COPY_BYTES = 256 << 20         # read (and written) by the traffic-calibration copy
 KERNEL_SOURCES = ["q4_group_quantized_amd/csrc/q4_gemv.hip",
                   "q4_group_quantized_amd/csrc/q4_device.hpp"]
 
@@ -88,6 +103,94 @@ def rocprof_summary(path: str) -> None:
         print("%-10s %-8d %-12.0f %-12d %s" % (grid, len(d), sum(d) / len(d), min(d), short))
 
 
+def _counter_rows(path: str):
+    """(kernel name, counter name, value) per dispatch from a rocprofv3 --pmc
+    counter_collection.csv."""
+    import csv
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            yield row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])
+
+
+def _counter_avg(path: str, counter: str, key: str) -> float:
+    vals = [v for name, c, v in _counter_rows(path) if c == counter and key in name]
+    if not vals:
+        raise SystemExit("no %s readings for a kernel matching %r in %s" % (counter, key, path))
+    return sum(vals) / len(vals)
+
+
+def read_traffic_file() -> dict:
+    out = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    out[k.strip()] = v.strip()
+    return out
+
+
+def traffic_record(fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per LM-head GEMV launch from FETCH_SIZE / WRITE_SIZE (KiB),
+    each calibrated on the copy kernel's known bytes."""
+    import q4_inputs as qi
+    g_fetch = _counter_avg(fetch_csv, "FETCH_SIZE", "gemv")
+    c_fetch = _counter_avg(fetch_csv, "FETCH_SIZE", "neg")
+    g_write = _counter_avg(write_csv, "WRITE_SIZE", "gemv")
+    c_write = _counter_avg(write_csv, "WRITE_SIZE", "neg")
+    f_fetch = COPY_BYTES / (c_fetch * 1024.0)
+    f_write = COPY_BYTES / (c_write * 1024.0)
+    mat = qi.DECODE_08B[-1]
+    algo = qi.workload_bytes(1, mat.n, mat.k)
+    traffic = g_fetch * 1024.0 * f_fetch + g_write * 1024.0 * f_write
+    lines = [
+        "# HBM traffic of one q4_gemv launch on the 0.8B LM head (m=1, n=%d, k=%d)" % (mat.n, mat.k),
+        "# Commands (repository root on the GPU host; one counter per run):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmcf "
+        "-o f --output-format csv -- python3 $REPO/bench.py --traffic-probe",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmcw "
+        "-o w --output-format csv -- python3 $REPO/bench.py --traffic-probe",
+        "#   python3 bench.py --traffic-record gpurun_out/pmcf/f_counter_collection.csv "
+        "gpurun_out/pmcw/w_counter_collection.csv",
+        "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the probe's launches),",
+        "# each scaled by the factor that maps the same counter's reading for a plain",
+        "# elementwise copy (torch.neg, %d bytes read and %d written) onto its known size." % (COPY_BYTES, COPY_BYTES),
+        "kernel_source_hash: %s" % kernel_source_hash(),
+        "gemv_fetch_kib: %.1f" % g_fetch,
+        "gemv_write_kib: %.1f" % g_write,
+        "copy_fetch_kib: %.1f" % c_fetch,
+        "copy_write_kib: %.1f" % c_write,
+        "fetch_factor: %.5f" % f_fetch,
+        "write_factor: %.5f" % f_write,
+        "bytes_per_launch: %d" % round(traffic),
+        "algorithmic_bytes_per_launch: %d" % algo,
+        "traffic_over_algorithmic: %.4f" % (traffic / algo),
+    ]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_probe() -> int:
+    import torch
+    import q4_group_quantized_amd as q4
+    import q4_inputs as qi
+    lib = q4.load()
+    mat = qi.DECODE_08B[-1]
+    x = torch.from_numpy(qi.activations(1, mat.k)).cuda()
+    p = Product(torch, q4, mat, 1, x, 1)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sh = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    for _ in range(3):
+        launch(lib, "q4_gemv", p.args(0), sh)
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("traffic probe: 3 LM-head GEMVs and 3 copies of %d bytes done" % COPY_BYTES)
+    return 0
+
+
 # --------------------------------------------------------------------------
 # GPU helpers
 # --------------------------------------------------------------------------
@@ -123,18 +226,12 @@ def launch(lib, fn, args, stream):
         raise RuntimeError("%s failed with status %d" % (fn, st))
 
 
-def time_launches(torch, lib, fn, prod, iters, stream_handle, per_launch_events):
-    """Average duration (s) of `iters` launches rotating through the copies."""
+def time_launches(torch, lib, fn, prod, iters, stream_handle):
+    """Average duration (s) of `iters` back-to-back launches rotating through
+    the weight copies: HIP events on the launching stream around the batch."""
+    for i in range(3):
+        launch(lib, fn, prod.args(i), stream_handle)
     torch.cuda.synchronize()
-    if per_launch_events:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(iters)]
-        for i in range(iters):
-            evs[i][0].record()
-            launch(lib, fn, prod.args(i), stream_handle)
-            evs[i][1].record()
-        torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / iters / 1e3
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(iters):
@@ -144,10 +241,47 @@ def time_launches(torch, lib, fn, prod, iters, stream_handle, per_launch_events)
     return a.elapsed_time(b) / iters / 1e3
 
 
-def decode_set(torch, q4, lib, workload, warmup, steps):
-    """Build a decode set, capture one graph per weight copy, time K steps."""
+# Matrices of a decode set that read the same input in the model: the
+# DeltaNet q/k/v projections of a layer, the attention q/k/v projections of a
+# layer, and the LM head (final hidden state).
+DECODE_GROUPS = ((0, 1, 2), (3, 4, 5), (6,))
+
+
+class MultiArgs:
+    """Host arrays of one q4_gemv_multi call (kept alive for graph capture)."""
+
+    def __init__(self, prods, c):
+        import ctypes
+        cnt = len(prods)
+        ptrs = ctypes.c_void_p * cnt
+        self.x = prods[0].x
+        self.k = prods[0].mat.k
+        self.count = cnt
+        self.packed = ptrs(*[p.copies[c % len(p.copies)][0].data_ptr() for p in prods])
+        self.scales = ptrs(*[p.copies[c % len(p.copies)][1].data_ptr() for p in prods])
+        self.y = ptrs(*[p.y.data_ptr() for p in prods])
+        self.n = (ctypes.c_int64 * cnt)(*[p.mat.n for p in prods])
+
+    def call(self, lib, stream):
+        st = lib.q4_gemv_multi(self.x.data_ptr(), 1, self.k, self.count, self.packed,
+                               self.scales, self.y, self.n, stream)
+        if st != 0:
+            raise RuntimeError("q4_gemv_multi failed with status %d" % st)
+
+
+def decode_set(torch, q4, lib, workload, warmup, steps, side_steps):
+    """Build a decode set and time one decode pass three ways, each replayed
+    from HIP graphs (one graph per weight copy):
+      grouped     one q4_gemv_multi per group of matrices sharing an input
+                  (DECODE_GROUPS) -- the step `value` is measured on
+      per_matrix  seven q4_gemv launches
+      fused       one q4_gemv_multi over all seven (the synthetic set shares x)
+    """
     import q4_inputs as qi
     mats = [mat for mat, _ in workload.cases]
+    names = [m.name.split(".")[1] for m in mats]
+    assert names == ["deltanet_q", "deltanet_k", "deltanet_v", "attn_q", "attn_k", "attn_v",
+                     "lm_head"], names
     k = mats[0].k
     x = torch.from_numpy(qi.activations(1, k, outliers=workload.outliers)).cuda()
     set_weight_bytes = sum(m.n * m.k // 2 + m.n * (m.k // 32) * 2 for m in mats)
@@ -158,52 +292,82 @@ def decode_set(torch, q4, lib, workload, warmup, steps):
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    # eager reference results of copy 0, then one graph per copy
-    for p in prods:
-        launch(lib, "q4_gemv", p.args(0), sh)
+    def per_matrix(c, h):
+        for p in prods:
+            launch(lib, "q4_gemv", p.args(c), h)
+
+    multi = {c: [MultiArgs([prods[i] for i in g], c) for g in DECODE_GROUPS]
+             for c in range(copies)}
+    fused = {c: MultiArgs(prods, c) for c in range(copies)}
+
+    def grouped(c, h):
+        for a in multi[c]:
+            a.call(lib, h)
+
+    def fused_one(c, h):
+        fused[c].call(lib, h)
+
+    # eager reference results of copy 0; every mode's graphs must reproduce it
+    per_matrix(0, sh)
     torch.cuda.synchronize()
     eager = [p.y.clone() for p in prods]
-    graphs = []
     cap = torch.cuda.Stream()
     cap.wait_stream(stream)
-    for c in range(copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            h = torch.cuda.current_stream().cuda_stream
+    results = {}
+    for mode, fn, nsteps in (("grouped", grouped, steps), ("per_matrix", per_matrix, side_steps),
+                             ("fused", fused_one, side_steps)):
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                fn(c, torch.cuda.current_stream().cuda_stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for c in range(copies):
             for p in prods:
-                launch(lib, "q4_gemv", p.args(c), h)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    # every copy's graph must reproduce the eager result bit for bit
-    for c in range(copies):
-        for p in prods:
-            p.y.zero_()
+                p.y.zero_()
+            torch.cuda.synchronize()
+            graphs[c].replay()
+            torch.cuda.synchronize()
+            for p, e in zip(prods, eager):
+                if not torch.equal(p.y, e):
+                    raise RuntimeError("%s graph of copy %d differs from the eager run"
+                                       % (mode, c))
+        for i in range(warmup):
+            graphs[i % copies].replay()
         torch.cuda.synchronize()
-        graphs[c].replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(nsteps):
+            graphs[i % copies].replay()
+        b.record()
         torch.cuda.synchronize()
-        for p, e in zip(prods, eager):
-            if not torch.equal(p.y, e):
-                raise RuntimeError("graph replay of copy %d differs from eager run" % c)
-
-    for i in range(warmup):
-        graphs[i % copies].replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(steps):
-        graphs[i % copies].replay()
-    b.record()
-    torch.cuda.synchronize()
-    step_s = a.elapsed_time(b) / steps / 1e3
+        results[mode] = a.elapsed_time(b) / nsteps / 1e3
+        del graphs
     set_bytes = sum(p.bytes for p in prods)
     per = []
     for p in prods:
-        t = time_launches(torch, lib, "q4_gemv", p, max(50, 2 * copies), sh, True)
+        t = time_launches(torch, lib, "q4_gemv", p, max(100, 4 * copies), sh)
         per.append({"matrix": p.mat.name, "n": p.mat.n, "k": p.mat.k, "us": round(t * 1e6, 3),
                     "GB_s": round(p.bytes / t / 1e9, 1),
                     "hbm_frac": round(p.bytes / t / 1e9 / HBM_PEAK_GBS, 4)})
-    return {"prods": prods, "step_s": step_s, "set_bytes": set_bytes, "per_matrix": per,
-            "copies": copies}
+    return {"prods": prods, "step_s": results["grouped"], "modes_s": results,
+            "set_bytes": set_bytes, "per_matrix": per, "copies": copies}
+
+
+def lm_head_rate(torch, q4, lib, mat, iters):
+    """Back-to-back m = 1 LM-head GEMVs over rotated weight copies."""
+    import q4_inputs as qi
+    x = torch.from_numpy(qi.activations(1, mat.k)).cuda()
+    copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 9 // 16)))
+    p = Product(torch, q4, mat, 1, x, copies)
+    t = time_launches(torch, lib, "q4_gemv", p, iters, torch.cuda.current_stream().cuda_stream)
+    out = {"matrix": mat.name, "n": mat.n, "k": mat.k, "us": round(t * 1e6, 3),
+           "GB_s": round(p.bytes / t / 1e9, 1),
+           "hbm_frac": round(p.bytes / t / 1e9 / HBM_PEAK_GBS, 4), "copies": copies}
+    del p
+    torch.cuda.empty_cache()
+    return out
 
 
 def gemm_case(torch, q4, lib, mat, m, outliers, iters):
@@ -213,8 +377,7 @@ def gemm_case(torch, q4, lib, mat, m, outliers, iters):
     p = Product(torch, q4, mat, m, x, copies)
     fn = "q4_gemv" if m <= 8 else "q4_gemm"
     sh = torch.cuda.current_stream().cuda_stream
-    time_launches(torch, lib, fn, p, 5, sh, False)
-    t = time_launches(torch, lib, fn, p, iters, sh, False)
+    t = time_launches(torch, lib, fn, p, iters, sh)
     out = {"matrix": mat.name, "m": m, "n": mat.n, "k": mat.k, "fn": fn, "us": round(t * 1e6, 3),
            "TFLOP_s": round(p.flops / t / 1e12, 2),
            "mfma_frac": round(p.flops / t / 1e12 / FP16_MFMA_PEAK_TFS, 4),
@@ -292,9 +455,14 @@ def main() -> int:
     ap.add_argument("--all", action="store_true", help="also time the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rocprof-summary", metavar="TRACE_CSV_OR_DB")
+    ap.add_argument("--traffic-probe", action="store_true")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return 0
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -310,25 +478,27 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.traffic_probe:
+        return traffic_probe()
     lib = q4.load()
     torch.cuda.set_device(0)
 
     wl = qi.WORKLOADS["decode_08b"]
+    side = max(50, args.steps // 4)
     log("decode set 0.8B: building")
-    ds = decode_set(torch, q4, lib, wl, args.warmup, args.steps)
+    ds = decode_set(torch, q4, lib, wl, args.warmup, args.steps, side)
     value = ds["set_bytes"] / ds["step_s"] / 1e9
 
-    # dominant kernel: the LM-head GEMV, per-launch HIP events (cold, rotating copies)
+    # dominant kernel: the LM-head GEMV, back-to-back launches over the
+    # rotated copies, HIP events on the launching stream around the batch
     lm = ds["prods"][-1]
     sh = torch.cuda.current_stream().cuda_stream
-    lm_t = time_launches(torch, lib, "q4_gemv", lm, max(200, 4 * ds["copies"]), sh, True)
+    lm_t = time_launches(torch, lib, "q4_gemv", lm, max(200, 8 * ds["copies"]), sh)
     achieved = lm.bytes / lm_t / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as fh:
-            tr = json.load(fh)
-        if tr.get("kernel_source_hash") == kernel_source_hash():
-            traffic = tr.get("bytes_per_launch")
+    tr = read_traffic_file()
+    if tr.get("kernel_source_hash") == kernel_source_hash() and "bytes_per_launch" in tr:
+        traffic = int(tr["bytes_per_launch"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "q4_gemv LM head m=1 n=248320 k=1024",
@@ -336,17 +506,23 @@ def main() -> int:
     del ds["prods"], lm
     torch.cuda.empty_cache()
 
-    detail = {"decode_08b_per_matrix": ds["per_matrix"], "rotation_copies": ds["copies"]}
+    def modes(d):
+        return {m: {"us_per_step": round(t * 1e6, 2),
+                    "GB_s": round(d["set_bytes"] / t / 1e9, 1)} for m, t in d["modes_s"].items()}
+
+    detail = {"decode_08b_modes": modes(ds), "decode_08b_per_matrix": ds["per_matrix"],
+              "rotation_copies": ds["copies"]}
+    log("LM head 4B")
+    detail["lm_head_4b"] = lm_head_rate(torch, q4, lib, qi.DECODE_4B[-1], 100)
     log("prefill GEMM M=512")
     detail["gemm_m512"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
     log("quantize 0.8B LM head")
     detail["quantize_lm_head_08b"] = quantize_rate(torch, q4, qi.DECODE_08B[-1], 10)
     if args.all:
         log("decode set 4B")
-        d4 = decode_set(torch, q4, lib, qi.WORKLOADS["decode_4b"], args.warmup, args.steps)
-        detail["decode_4b"] = {"GB_s": round(d4["set_bytes"] / d4["step_s"] / 1e9, 1),
-                               "us_per_step": round(d4["step_s"] * 1e6, 2),
-                               "per_matrix": d4["per_matrix"]}
+        d4 = decode_set(torch, q4, lib, qi.WORKLOADS["decode_4b"], args.warmup, side, side)
+        detail["decode_4b_modes"] = modes(d4)
+        detail["decode_4b_per_matrix"] = d4["per_matrix"]
         del d4
         torch.cuda.empty_cache()
         for m in (16, 128, 2048):
@@ -374,9 +550,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16xq4->f32",
         "data": "synthetic",
-        "config": {"workload": "0.8B-shaped Q4 decode set, M=1, K=1024 (7 GEMVs incl. "
-                               "248320-row LM head), weights rotated over %d copies"
-                               % ds["copies"],
+        "config": {"workload": "0.8B-shaped Q4 decode set, M=1, K=1024 (7 matrices incl. "
+                               "248320-row LM head) as 3 launches: DeltaNet q/k/v and "
+                               "attention q/k/v each one q4_gemv_multi, LM head; weights "
+                               "rotated over %d copies" % ds["copies"],
                    "m": 1, "k": 1024, "n": [mat.n for mat, _ in wl.cases],
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,

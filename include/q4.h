@@ -57,8 +57,9 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 1
+#define Q4_ABI_VERSION 2
 #define Q4_GROUP 32
+#define Q4_MULTI_MAX 8
 
 typedef enum {
     Q4_OK = 0,
@@ -105,6 +106,30 @@ q4_status q4_quantize(const float* w, uint8_t* packed, uint16_t* scales,
 q4_status q4_gemv(const uint16_t* x, const uint8_t* packed,
                   const uint16_t* scales, float* y,
                   int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * q4_gemv_multi -- several decode products over the SAME activations in one
+ * call: y_i = x * dequant(W_i)^T for i < count, every W_i with the same k.
+ * Projections that read one input are such a set: the fused gate+up GEMV of
+ * the QORA-LLM-0.8B card ("AVX-512 SIMD Acceleration"), and the q/k/v
+ * projections of one layer input in the hybrid DeltaNet/attention stack
+ * ("Architecture" table of the same card).  One launch serves the whole set
+ * at m = 1, so the fixed cost of a kernel is paid once, not per matrix.
+ *   x       [in]  fp16 bits [m, k], device, 1 <= m <= 8
+ *   count         number of matrices, 1 .. Q4_MULTI_MAX
+ *   packed  [in]  HOST array of count device pointers, uint8 [n[i], k/2]
+ *   scales  [in]  HOST array of count device pointers, fp16 bits [n[i], k/32]
+ *   y       [out] HOST array of count device pointers, fp32 [m, n[i]]
+ *   n       [in]  HOST array of count row counts
+ * The host arrays are read during the call only.  Every matrix follows the
+ * shape and alignment rules of q4_gemv; count outside 1..Q4_MULTI_MAX ->
+ * Q4_ERR_SHAPE; a NULL array or element -> Q4_ERR_NULL.  The outputs must
+ * not overlap each other or any input (not checked).  Each y[i] is
+ * bit-identical to what q4_gemv returns for matrix i alone.
+ */
+q4_status q4_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
+                        const uint8_t* const* packed, const uint16_t* const* scales,
+                        float* const* y, const int64_t* n, void* stream);
 
 /*
  * q4_gemm -- prefill product, same arguments and semantics as q4_gemv, for

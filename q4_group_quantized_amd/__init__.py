@@ -9,6 +9,7 @@ Functions keep the C names:
   q4_quantize(w)                       -> (packed uint8 [n,k/2], scales fp16 [n,k/32])
   q4_gemv(x, packed, scales)           -> y fp32 [m,n]     (1 <= m <= 8)
   q4_gemm(x, packed, scales)           -> y fp32 [m,n]     (any m >= 1)
+  q4_gemv_multi(x, [(packed, scales), ...]) -> [y_i fp32 [m,n_i]]  (shared x, <= 8 matrices)
   q4_status_str(code), q4_abi_version()
 Outputs may be passed in (``out=``) to avoid allocation.
 """
@@ -21,9 +22,11 @@ from typing import Optional, Tuple
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4.so")
 
-EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm")
+EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm",
+            "q4_gemv_multi")
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE = range(6)
 GROUP = 32
+MULTI_MAX = 8
 
 
 class Q4Error(RuntimeError):
@@ -55,6 +58,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [p, p, p, p, i64, i64, i64, p]
         fn.restype = ctypes.c_int
+    lib.q4_gemv_multi.argtypes = [p, i64, i64, ctypes.c_int32, p, p, p, p, p]
+    lib.q4_gemv_multi.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -140,3 +145,42 @@ def q4_gemv(x, packed, scales, out=None, stream=None):
 def q4_gemm(x, packed, scales, out=None, stream=None):
     """Prefill product for any m >= 1 (tuned for m >= 16)."""
     return _product("q4_gemm", x, packed, scales, out, stream)
+
+
+def q4_gemv_multi(x, mats, out=None, stream=None):
+    """Decode products of several matrices over the same x in one call.
+
+    mats: sequence of (packed, scales) pairs with the same k; returns the list
+    of y_i [m, n_i] (or fills ``out``, a list of fp32 [m, n_i] tensors)."""
+    import torch
+    _require(x, torch.float16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
+    m, k = x.shape
+    count = len(mats)
+    if out is not None and len(out) != count:
+        raise ValueError("out must hold one tensor per matrix")
+    ys = []
+    for i, (packed, scales) in enumerate(mats):
+        _require(packed, torch.uint8, "packed[%d]" % i)
+        _require(scales, torch.float16, "scales[%d]" % i)
+        n = packed.shape[0]
+        if packed.dim() != 2 or packed.shape[1] * 2 != k or tuple(scales.shape) != (n, k // GROUP):
+            raise ValueError("matrix %d: shapes disagree with x %s" % (i, tuple(x.shape)))
+        if out is None:
+            ys.append(torch.empty((m, n), dtype=torch.float32, device=x.device))
+        else:
+            _require(out[i], torch.float32, "out[%d]" % i)
+            if tuple(out[i].shape) != (m, n):
+                raise ValueError("out[%d] must be [m, n]" % i)
+            ys.append(out[i])
+    ptrs = ctypes.c_void_p * max(count, 1)
+    packed_a = ptrs(*[p.data_ptr() for p, _ in mats])
+    scales_a = ptrs(*[s.data_ptr() for _, s in mats])
+    y_a = ptrs(*[y.data_ptr() for y in ys])
+    n_a = (ctypes.c_int64 * max(count, 1))(*[p.shape[0] for p, _ in mats])
+    with torch.cuda.device(x.device):
+        st = load().q4_gemv_multi(x.data_ptr(), m, k, count, packed_a, scales_a, y_a, n_a,
+                                  _stream(stream, x.device))
+    _check("q4_gemv_multi", st)
+    return ys

@@ -90,7 +90,7 @@ const char* q4_status_str(q4_status status) {
     switch (status) {
         case Q4_OK: return "ok";
         case Q4_ERR_NULL: return "null pointer argument";
-        case Q4_ERR_SHAPE: return "shape out of range (need n>=1, k>=32, k%32==0, m in range)";
+        case Q4_ERR_SHAPE: return "shape out of range (need n>=1, k>=32, k%32==0, m and count in range)";
         case Q4_ERR_ALIGN: return "misaligned pointer (x, packed, w: 16 B; scales: 2 B; y: 4 B)";
         case Q4_ERR_LAUNCH: return "kernel launch failed";
         case Q4_ERR_DEVICE: return "current device is not a usable gfx950";
@@ -116,6 +116,21 @@ q4_status q4_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* scal
     if ((st = device_ok()) != Q4_OK) return st;
     return map_launch(q4::launch_gemv(x, packed, scales, y, m, n, k,
                                       static_cast<hipStream_t>(stream)));
+}
+
+q4_status q4_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
+                        const uint8_t* const* packed, const uint16_t* const* scales,
+                        float* const* y, const int64_t* n, void* stream) {
+    if (!packed || !scales || !y || !n) return Q4_ERR_NULL;
+    if (count < 1 || count > Q4_MULTI_MAX) return Q4_ERR_SHAPE;
+    for (int32_t i = 0; i < count; ++i) {
+        const q4_status st = check_product(x, packed[i], scales[i], y[i], m, n[i], k, 8);
+        if (st != Q4_OK) return st;
+    }
+    q4_status st = device_ok();
+    if (st != Q4_OK) return st;
+    return map_launch(q4::launch_gemv_multi(x, m, k, count, packed, scales, y, n,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 q4_status q4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* scales, float* y,

@@ -68,9 +68,12 @@ struct SpliceConsts {
     uint32_t mask;       // kNibblePairMask
     uint32_t magic;      // kMagic1024x2
     uint32_t sel[4];     // byte selectors of unpack8_natural
+    uint32_t mask16;     // kNibblePairMask16
 };
+constexpr uint32_t kNibblePairMask16 = 0x00F000F0u;
 constexpr SpliceConsts kSpliceConsts = {kNibblePairMask, kMagic1024x2,
-                                        {0x0C040C00u, 0x0C050C01u, 0x0C060C02u, 0x0C070C03u}};
+                                        {0x0C040C00u, 0x0C050C01u, 0x0C060C02u, 0x0C070C03u},
+                                        kNibblePairMask16};
 
 // A kernel-argument value copied into a VGPR (identity DPP move): with the
 // mask in an SGPR and the magic in a VGPR the splice is one v_and_or_b32
@@ -89,6 +92,27 @@ __device__ __forceinline__ void unpack8_pairs(uint32_t d, uint32_t mask, uint32_
     h[1] = as_half2(((d >> 4) & mask) | magic) + bias;
     h[2] = as_half2(((d >> 8) & mask) | magic) + bias;
     h[3] = as_half2(((d >> 12) & mask) | magic) + bias;
+}
+
+// The table lookup with one shift fewer, for v_dot2_f32_f16 with two sums.
+// Codes at bits 4..7 of a byte are spliced where they stand: bits 4..7 of the
+// mantissa of 1024.0 weigh 16 each, so (d & 0x00F000F0) | 0x64006400 is
+// 1024 + 16 v, and subtracting 1152 leaves 16 (v - 8), exact.  Codes at bits
+// 0..3 give v - 8 as in unpack8_pairs.  Output, as (lo half, hi half) pairs:
+//   lo[0] = (e0, e4) levels        hi[0] = 16 x (e1, e5) levels
+//   lo[1] = (e2, e6) levels        hi[1] = 16 x (e3, e7) levels
+// The caller sums lo and hi products separately and forms lo + hi / 16, which
+// is exact scaling, so every product stays the exact x * level product.
+__device__ __forceinline__ void unpack8_split(uint32_t d, uint32_t mask, uint32_t mask16,
+                                              uint32_t magic, half2_t (&lo)[2],
+                                              half2_t (&hi)[2]) {
+    const half2_t bias1 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2_t bias16 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const uint32_t d8 = d >> 8;
+    lo[0] = as_half2((d & mask) | magic) + bias1;
+    hi[0] = as_half2((d & mask16) | magic) + bias16;
+    lo[1] = as_half2((d8 & mask) | magic) + bias1;
+    hi[1] = as_half2((d8 & mask16) | magic) + bias16;
 }
 
 // The table lookup in natural element order, for operands whose activations

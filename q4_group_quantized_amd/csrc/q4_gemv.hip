@@ -34,12 +34,16 @@
 // m = 1 has its own streaming kernel (gemv1_kernel below): there the block-
 // diagonal MFMA would waste 15/16 of the matrix core anyway, and what bounds
 // the kernel is how sequentially each wave walks HBM.  Every wave owns a
-// contiguous range of rows and reads it front to back; LPR = 8, 16 or 32
-// lanes share a row, each lane owning the same GPL = K / (32 LPR) groups of
-// every row, so its activations stay in registers for the whole kernel.
-// Per group: 16-byte code load, the 16-entry table lookup as four fp16 pairs,
-// four v_dot2_f32_f16 against the matching activation pairs, then the fp32
-// scale; the 16 per-lane partial sums of a row are added with DPP rotations.
+// contiguous range of rows and reads it front to back, one wave per SIMD;
+// LPR = 16, 8 or 32 lanes share a row, each lane owning the same
+// GPL = K / (32 LPR) groups of every row, so its activations stay in
+// registers for the whole kernel.  Per group: 16-byte code load, the 16-entry
+// table lookup as fp16 pairs (unpack8_split), v_dot2_f32_f16 against the
+// matching activation pairs into two fp32 sums, then the fp32 scale; the
+// per-lane partial sums of a row are added with DPP rotations.  The same
+// kernel serves several matrices that share x (q4_gemv_multi) from a table
+// of segments, so a set of projections costs one launch.
+#include "q4.h"
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
 
@@ -351,23 +355,78 @@ __device__ __forceinline__ float lanes_sum(float v) {
     }
 }
 
-// LPR lanes share a row (64 / LPR rows per wave step); lane `sub` owns groups
-// sub + LPR * i, i < GPL, of every row, so G = LPR * GPL.  PF steps in flight.
+// The matrices of one m = 1 launch: up to kGemv1MaxSegments weight matrices
+// that share x and K (one matrix for q4_gemv).  The host splits the waves
+// between them in proportion to their rows; wave w of segment s (w counted
+// from wave0[s]) owns row quads [w * base + min(w, extra), +base + (w < extra)).
+constexpr int kGemv1MaxSegments = 8;
+struct Gemv1Segments {
+    const uint8_t* packed[kGemv1MaxSegments];
+    const uint16_t* scales[kGemv1MaxSegments];
+    float* y[kGemv1MaxSegments];
+    int64_t n[kGemv1MaxSegments];
+    int64_t wave0[kGemv1MaxSegments];
+    int64_t waves[kGemv1MaxSegments];
+    int64_t base[kGemv1MaxSegments];
+    int64_t extra[kGemv1MaxSegments];
+    int count;
+};
+static_assert(kGemv1MaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MULTI_MAX matrices");
+
+// LPR lanes share a row (RPS = 64 / LPR rows per wave step); lane `sub` owns
+// groups sub + LPR * i, i < GPL, of every row, so G = LPR * GPL.  Each wave
+// walks its own contiguous rows front to back with PF steps of loads in
+// flight.  Refill loads past the wave's last step re-read that last step
+// (this wave's own rows, still cached), so every load is unconditional and
+// the compiler keeps PF steps outstanding instead of draining the queue; the
+// last PF steps are computed after the loop without new loads.
 template <int LPR, int GPL, int PF>
 __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, float* __restrict__ y, int64_t N, int K,
-    int64_t RQ, SpliceConsts kc) {
-    constexpr int RPS = 64 / LPR;                       // rows per wave step
+    const uint16_t* __restrict__ x, int K, Gemv1Segments seg, SpliceConsts kc) {
+    constexpr int RPS = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int sub = lane % LPR;
     const int r = lane / LPR;
     const int G = K / 32;
-    const int64_t W = (int64_t)gridDim.x * kGemvWaves;
-    const int64_t w = (int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6);
-    const int64_t base = RQ / W, extra = RQ % W;
-    const int64_t q0 = w * base + (w < extra ? w : extra);
-    const int64_t cnt = base + (w < extra ? 1 : 0);
+    const int64_t w = (int64_t)blockIdx.x * kGemvWaves +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // this wave's segment (wave-uniform selects over constant indices)
+    const uint8_t* packed = seg.packed[0];
+    const uint16_t* scales = seg.scales[0];
+    float* y = seg.y[0];
+    int64_t N = seg.n[0], wave0 = seg.wave0[0], waves = seg.waves[0];
+    int64_t base = seg.base[0], extra = seg.extra[0];
+#pragma unroll
+    for (int i = 1; i < kGemv1MaxSegments; ++i) {
+        if (i < seg.count && w >= seg.wave0[i]) {
+            packed = seg.packed[i]; scales = seg.scales[i]; y = seg.y[i];
+            N = seg.n[i]; wave0 = seg.wave0[i]; waves = seg.waves[i];
+            base = seg.base[i]; extra = seg.extra[i];
+        }
+    }
+    const int64_t lw = w - wave0;
+    if (lw >= waves) return;
+    const int64_t q0 = lw * base + (lw < extra ? lw : extra);
+    const int64_t cnt = base + (lw < extra ? 1 : 0);
+    const int64_t row0 = RPS * q0 + r;
+
+    u32x4_t rp[PF][GPL];
+    uint32_t rs[PF][GPL];
+    auto load = [&](int slot, int64_t f) {
+        int64_t row = row0 + RPS * (f < cnt ? f : cnt - 1);
+        row = row < N ? row : N - 1;            // the segment's last quad may be partial
+        const uint8_t* pp = packed + row * (int64_t)(K / 2) + 16 * sub;
+        const uint16_t* sp = scales + row * (int64_t)G + sub;
+#pragma unroll
+        for (int i = 0; i < GPL; ++i) {
+            rp[slot][i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(pp + 16 * LPR * i));
+            rs[slot][i] = sp[LPR * i];
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load(p, p);
 
     // this lane's activations, as fp16 pairs in unpack order
     uint32_t xr[GPL][16];
@@ -381,114 +440,134 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
             for (int e = 0; e < 4; ++e) xr[i][4 * c + e] = v[e];
         }
 
-    // Loads stay unconditional so that PF steps remain in flight: steps past
-    // the wave's range, and rows past N, re-read row N-1, which every wave
-    // shares and the caches keep; those results are never stored.
-    const int64_t row0 = RPS * q0 + r;
-    const uint8_t* pbase = packed + row0 * (int64_t)(K / 2) + 16 * sub;
-    const uint16_t* sbase = scales + row0 * (int64_t)G + sub;
-    const uint8_t* plast = packed + (N - 1) * (int64_t)(K / 2) + 16 * sub;
-    const uint16_t* slast = scales + (N - 1) * (int64_t)G + sub;
-    const int64_t pstep = (int64_t)RPS * (K / 2);
-    const int64_t sstep = (int64_t)RPS * G;
-    u32x4_t rp[PF][GPL];
-    uint32_t rs[PF][GPL];
-    auto load = [&](int slot, int64_t f) {
-        const bool ok = f < cnt && row0 + RPS * f < N;
-        const uint8_t* pp = ok ? pbase + f * pstep : plast;
-        const uint16_t* sp = ok ? sbase + f * sstep : slast;
+    const uint32_t mask = kc.mask, mask16 = kc.mask16;
+    const uint32_t magic = to_vgpr(kc.magic);
+    // one step: this lane's GPL groups of its row, scaled and summed
+    auto compute = [&](int p) {
+        float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < GPL; ++i) {
-            rp[slot][i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t*>(pp + 16 * LPR * i));
-            rs[slot][i] = sp[LPR * i];
-        }
-    };
+            float lo = 0.f, hi = 0.f;
 #pragma unroll
-    for (int p = 0; p < PF; ++p) load(p, p);
+            for (int c = 0; c < 4; ++c) {
+                half2_t l[2], h[2];
+                unpack8_split(rp[p][i][c], mask, mask16, magic, l, h);
+                lo = __builtin_amdgcn_fdot2(l[0], as_half2(xr[i][4 * c + 0]), lo, false);
+                hi = __builtin_amdgcn_fdot2(h[0], as_half2(xr[i][4 * c + 1]), hi, false);
+                lo = __builtin_amdgcn_fdot2(l[1], as_half2(xr[i][4 * c + 2]), lo, false);
+                hi = __builtin_amdgcn_fdot2(h[1], as_half2(xr[i][4 * c + 3]), hi, false);
+            }
+            acc = fmaf(half_bits_to_float(rs[p][i]), fmaf(hi, 0.0625f, lo), acc);
+        }
+        return lanes_sum<LPR>(acc);
+    };
 
-    const uint32_t mask = kc.mask;
-    const uint32_t magic = to_vgpr(kc.magic);
-    for (int64_t f0 = 0; f0 < cnt; f0 += PF) {
+    int64_t f0 = 0;
+    for (; f0 + PF < cnt; f0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
-            const int64_t f = f0 + p;
-            float acc = 0.f;
+            const float acc = compute(p);
+            load(p, f0 + p + PF);
+            const int64_t row = row0 + RPS * (f0 + p);
+            if (sub == 0 && row < N) y[row] = acc;
+        }
+    }
 #pragma unroll
-            for (int i = 0; i < GPL; ++i) {
-                float dot = 0.f;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    half2_t h[4];
-                    unpack8_pairs(rp[p][i][c], mask, magic, h);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        dot = __builtin_amdgcn_fdot2(h[e], as_half2(xr[i][4 * c + e]), dot,
-                                                     false);
-                }
-                acc = fmaf(half_bits_to_float(rs[p][i]), dot, acc);
-            }
-            load(p, f + PF);
-            acc = lanes_sum<LPR>(acc);
-            const int64_t row = row0 + RPS * f;
-            if (f < cnt && sub == 0 && row < N) y[row] = acc;
+    for (int p = 0; p < PF; ++p) {
+        if (f0 + p < cnt) {
+            const float acc = compute(p);
+            const int64_t row = row0 + RPS * (f0 + p);
+            if (sub == 0 && row < N) y[row] = acc;
         }
     }
 }
 
+// Steps in flight per wave: about 16 code loads per lane outstanding.
+constexpr int gemv1_prefetch(int gpl) {
+    return gpl <= 2 ? 8 : gpl == 3 ? 6 : gpl <= 5 ? 4 : gpl <= 7 ? 3 : 2;
+}
+
+// One wave per SIMD: fewer, longer sequential streams measured faster than
+// more waves each with a shorter range.
 template <int LPR, int GPL>
-hipError_t launch_gemv1_t(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
-                          float* y, int64_t n, int k, hipStream_t stream) {
-    constexpr int PF = GPL <= 4 ? 4 : 2;
+hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* const* packed,
+                          const uint16_t* const* scales, float* const* y, const int64_t* n,
+                          hipStream_t stream) {
+    constexpr int PF = gemv1_prefetch(GPL);
+    constexpr int RPS = 64 / LPR;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    constexpr int RPS = 64 / LPR;
-    const int64_t RQ = (n + RPS - 1) / RPS;
-    static int blocks_per_cu = 0;               // occupancy of this instantiation
-    if (blocks_per_cu == 0) {
-        int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv1_kernel<LPR, GPL, PF>,
-                                                         kGemvThreads, 0) != hipSuccess ||
-            nb < 1)
-            nb = 1;
-        blocks_per_cu = nb;
+    Gemv1Segments seg = {};
+    seg.count = count;
+    int64_t total_rq = 0;
+    for (int s = 0; s < count; ++s) total_rq += (n[s] + RPS - 1) / RPS;
+    const int64_t max_waves = (int64_t)device_info(dev).cu_count * kGemvWaves;
+    const int64_t per = (total_rq + max_waves - 1) / max_waves;   // steps per wave
+    int64_t wave0 = 0;
+    for (int s = 0; s < count; ++s) {
+        const int64_t rq = (n[s] + RPS - 1) / RPS;
+        const int64_t waves = (rq + per - 1) / per;
+        seg.packed[s] = packed[s];
+        seg.scales[s] = scales[s];
+        seg.y[s] = y[s];
+        seg.n[s] = n[s];
+        seg.wave0[s] = wave0;
+        seg.waves[s] = waves;
+        seg.base[s] = rq / waves;
+        seg.extra[s] = rq % waves;
+        wave0 += waves;
     }
-    // as many waves as are resident at once, trimmed so that every wave gets
-    // the same number of steps
-    const int64_t max_waves = (int64_t)device_info(dev).cu_count * blocks_per_cu * kGemvWaves;
-    const int64_t per = (RQ + max_waves - 1) / max_waves;
-    const int64_t waves = (RQ + per - 1) / per;
-    const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
+    const int blocks = (int)((wave0 + kGemvWaves - 1) / kGemvWaves);
     hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF>), dim3(blocks), dim3(kGemvThreads), 0, stream,
-                       x, packed, scales, y, n, k, RQ, kSpliceConsts);
+                       x, k, seg, kSpliceConsts);
     return hipGetLastError();
 }
 
 template <int LPR>
-hipError_t launch_gemv1_lpr(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
-                            float* y, int64_t n, int k, hipStream_t stream) {
+hipError_t launch_gemv1_lpr(const uint16_t* x, int k, int count, const uint8_t* const* packed,
+                            const uint16_t* const* scales, float* const* y, const int64_t* n,
+                            hipStream_t stream) {
     switch ((k / 32) / LPR) {
-        case 1: return launch_gemv1_t<LPR, 1>(x, packed, scales, y, n, k, stream);
-        case 2: return launch_gemv1_t<LPR, 2>(x, packed, scales, y, n, k, stream);
-        case 3: return launch_gemv1_t<LPR, 3>(x, packed, scales, y, n, k, stream);
-        case 4: return launch_gemv1_t<LPR, 4>(x, packed, scales, y, n, k, stream);
-        case 5: return launch_gemv1_t<LPR, 5>(x, packed, scales, y, n, k, stream);
-        case 6: return launch_gemv1_t<LPR, 6>(x, packed, scales, y, n, k, stream);
-        case 7: return launch_gemv1_t<LPR, 7>(x, packed, scales, y, n, k, stream);
-        default: return launch_gemv1_t<LPR, 8>(x, packed, scales, y, n, k, stream);
+        case 1: return launch_gemv1_t<LPR, 1>(x, k, count, packed, scales, y, n, stream);
+        case 2: return launch_gemv1_t<LPR, 2>(x, k, count, packed, scales, y, n, stream);
+        case 3: return launch_gemv1_t<LPR, 3>(x, k, count, packed, scales, y, n, stream);
+        case 4: return launch_gemv1_t<LPR, 4>(x, k, count, packed, scales, y, n, stream);
+        case 5: return launch_gemv1_t<LPR, 5>(x, k, count, packed, scales, y, n, stream);
+        case 6: return launch_gemv1_t<LPR, 6>(x, k, count, packed, scales, y, n, stream);
+        case 7: return launch_gemv1_t<LPR, 7>(x, k, count, packed, scales, y, n, stream);
+        default: return launch_gemv1_t<LPR, 8>(x, k, count, packed, scales, y, n, stream);
     }
 }
 
-// Lanes per row for the m = 1 kernel, or 0 when k does not fit it.  Short
-// rows (k <= 1024) use 8 lanes per row so that each lane still owns 4 groups.
+// Lanes per row for the m = 1 kernel, or 0 when k does not fit it.
 int gemv1_lanes_per_row(int64_t k) {
     const int64_t G = k / 32;
-    if (G % 8 == 0 && G <= 32) return 8;
     if (G % 16 == 0 && G / 16 <= kGemv1MaxGpl) return 16;
     if (G % 8 == 0 && G / 8 <= kGemv1MaxGpl) return 8;
     if (G % 32 == 0 && G / 32 <= kGemv1MaxGpl) return 32;
     return 0;
+}
+
+hipError_t launch_gemv1(const uint16_t* x, int k, int count, const uint8_t* const* packed,
+                        const uint16_t* const* scales, float* const* y, const int64_t* n,
+                        hipStream_t stream) {
+    switch (gemv1_lanes_per_row(k)) {
+        case 8: return launch_gemv1_lpr<8>(x, k, count, packed, scales, y, n, stream);
+        case 16: return launch_gemv1_lpr<16>(x, k, count, packed, scales, y, n, stream);
+        default: return launch_gemv1_lpr<32>(x, k, count, packed, scales, y, n, stream);
+    }
+}
+
+hipError_t launch_gemv_blockdiag(const uint16_t* x, const uint8_t* packed,
+                                 const uint16_t* scales, float* y, int64_t m, int64_t n,
+                                 int64_t k, hipStream_t stream) {
+    const bool s16 = ((k / 32) % 8) == 0;
+    if (m <= 4)
+        return s16 ? launch_gemv_t<1, true>(x, packed, scales, y, (int)m, n, (int)k, stream)
+                   : launch_gemv_t<1, false>(x, packed, scales, y, (int)m, n, (int)k, stream);
+    return s16 ? launch_gemv_t<2, true>(x, packed, scales, y, (int)m, n, (int)k, stream)
+               : launch_gemv_t<2, false>(x, packed, scales, y, (int)m, n, (int)k, stream);
 }
 
 }  // namespace
@@ -496,21 +575,21 @@ int gemv1_lanes_per_row(int64_t k) {
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed,
                        const uint16_t* scales, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
-    const int64_t G = k / 32;
-    if (m == 1) {
-        switch (gemv1_lanes_per_row(k)) {
-            case 8: return launch_gemv1_lpr<8>(x, packed, scales, y, n, (int)k, stream);
-            case 16: return launch_gemv1_lpr<16>(x, packed, scales, y, n, (int)k, stream);
-            case 32: return launch_gemv1_lpr<32>(x, packed, scales, y, n, (int)k, stream);
-            default: break;
-        }
+    if (m == 1 && gemv1_lanes_per_row(k) != 0)
+        return launch_gemv1(x, (int)k, 1, &packed, &scales, &y, &n, stream);
+    return launch_gemv_blockdiag(x, packed, scales, y, m, n, k, stream);
+}
+
+hipError_t launch_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int count,
+                             const uint8_t* const* packed, const uint16_t* const* scales,
+                             float* const* y, const int64_t* n, hipStream_t stream) {
+    if (m == 1 && gemv1_lanes_per_row(k) != 0)
+        return launch_gemv1(x, (int)k, count, packed, scales, y, n, stream);
+    for (int s = 0; s < count; ++s) {
+        const hipError_t e = launch_gemv_blockdiag(x, packed[s], scales[s], y[s], m, n[s], k, stream);
+        if (e != hipSuccess) return e;
     }
-    const bool s16 = (G % 8) == 0;
-    if (m <= 4)
-        return s16 ? launch_gemv_t<1, true>(x, packed, scales, y, (int)m, n, (int)k, stream)
-                   : launch_gemv_t<1, false>(x, packed, scales, y, (int)m, n, (int)k, stream);
-    return s16 ? launch_gemv_t<2, true>(x, packed, scales, y, (int)m, n, (int)k, stream)
-               : launch_gemv_t<2, false>(x, packed, scales, y, (int)m, n, (int)k, stream);
+    return hipSuccess;
 }
 
 }  // namespace q4

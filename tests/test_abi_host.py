@@ -103,7 +103,48 @@ def test_gemv_rejects_more_than_eight_rows(lib):
     assert lib.q4_gemv(FAKE, FAKE, FAKE, FAKE, 9, 8, 64, None) == 2
 
 
+def _multi(lib, x, m, k, packed, scales, y, n, count=None):
+    """Call q4_gemv_multi with host arrays built from Python lists (None = NULL array)."""
+    def arr(vals, ctype):
+        return None if vals is None else (ctype * max(len(vals), 1))(*vals)
+    cnt = len(n) if count is None else count
+    return lib.q4_gemv_multi(x, m, k, cnt, arr(packed, ctypes.c_void_p),
+                             arr(scales, ctypes.c_void_p), arr(y, ctypes.c_void_p),
+                             arr(n, ctypes.c_int64), None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(packed=None), 1),
+    (dict(scales=None), 1),
+    (dict(y=None), 1),
+    (dict(n=None, count=2), 1),
+    (dict(x=None), 1),
+    (dict(packed=[FAKE, NULL]), 1),
+    (dict(scales=[NULL, FAKE]), 1),
+    (dict(y=[FAKE, NULL]), 1),
+    (dict(count=0), 2),
+    (dict(count=9, packed=[FAKE] * 9, scales=[FAKE] * 9, y=[FAKE] * 9, n=[8] * 9), 2),
+    (dict(count=-1), 2),
+    (dict(m=0), 2),
+    (dict(m=9), 2),
+    (dict(k=48), 2),
+    (dict(n=[8, 0]), 2),
+    (dict(n=[8, 2 ** 31]), 2),
+    (dict(x=FAKE + 2), 3),
+    (dict(packed=[FAKE, FAKE + 4]), 3),
+    (dict(scales=[FAKE + 1, FAKE]), 3),
+    (dict(y=[FAKE, FAKE + 2]), 3),
+])
+def test_gemv_multi_rejects_bad_arguments(lib, case, expect):
+    args = dict(x=FAKE, m=1, k=64, packed=[FAKE, FAKE], scales=[FAKE, FAKE], y=[FAKE, FAKE],
+                n=[8, 8], count=None)
+    args.update(case)
+    assert _multi(lib, **args) == expect
+
+
 def test_binding_names_match_the_c_abi():
     import q4_group_quantized_amd as q4
-    for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_status_str", "q4_abi_version"):
+    for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_gemv_multi", "q4_status_str",
+                 "q4_abi_version"):
         assert callable(getattr(q4, name))
+    assert set(q4.EXPORTED) == set(declared_functions())

@@ -209,6 +209,86 @@ def test_binding_rejects_bad_calls(q4):
 
 
 # --------------------------------------------------------------------------
+# several matrices over one x in one call (q4_gemv_multi)
+# --------------------------------------------------------------------------
+
+MULTI_SETS = [
+    (1, 1024, (1, 17, 300, 4099)),
+    (1, 2560, (61, 5, 1000, 3, 257, 64, 9, 2)),      # eight matrices, ragged rows
+    (1, 512, (1,)),
+    (1, 8192, (5, 61)),
+    (1, 96, (17, 33)),                               # k outside the streaming kernel
+    (2, 256, (15, 100)),
+    (8, 1056, (33, 7, 64)),
+]
+
+
+@pytest.mark.parametrize("m,k,ns", MULTI_SETS, ids=["m%d-k%d-%dmat" % (c[0], c[1], len(c[2]))
+                                                    for c in MULTI_SETS])
+def test_gemv_multi(q4, orc, m, k, ns):
+    """Each output against the oracle, and bit-identical to q4_gemv alone."""
+    rng = np.random.default_rng(m * 7 + k + len(ns))
+    x = (rng.standard_normal((m, k)) * 2).astype(np.float16)
+    mats, refs = [], []
+    for i, n in enumerate(ns):
+        w = oracle_pins.spread_weights(rng, n, k) if i % 2 else \
+            (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        packed, scales = orc.quantize(w)
+        mats.append((gpu(packed), gpu(scales.view(np.float16))))
+        refs.append(orc.matmul(x, packed, scales))
+    _log("q4_gemv_multi m=%d k=%d n=%s" % (m, k, ns))
+    xg = gpu(x)
+    ys = q4.q4_gemv_multi(xg, mats)
+    torch.cuda.synchronize()
+    for i, (y, (y_ref, bound)) in enumerate(zip(ys, refs)):
+        assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound,
+                      "multi matrix %d (n=%d)" % (i, ns[i]))
+        alone = q4.q4_gemv(xg, *mats[i])
+        torch.cuda.synchronize()
+        assert torch.equal(y, alone), "multi matrix %d differs from q4_gemv" % i
+
+
+def test_gemv_multi_binding_errors(q4):
+    x = torch.zeros((1, 64), dtype=torch.float16, device=DEV)
+    p = torch.zeros((4, 32), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((4, 2), dtype=torch.float16, device=DEV)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv_multi(x, [])
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv_multi(x, [(p, s)] * 9)
+    with pytest.raises(ValueError):
+        q4.q4_gemv_multi(x, [(p, s), (p[:, :16], s[:, :1])])
+
+
+@pytest.mark.parametrize("key", ["decode_08b", "decode_4b"])
+def test_gemv_multi_decode_set_full_size(q4, orc, key):
+    """A whole decode set (seven matrices incl. the LM head) in one call, at
+    full size: sampled rows against the oracle, every output bit-identical to
+    q4_gemv on that matrix alone."""
+    wl = qi.WORKLOADS[key]
+    x = qi.activations(1, wl.cases[0][0].k, outliers=wl.outliers)
+    xg = gpu(x)
+    mats, samples = [], []
+    for mat, _ in wl.cases:
+        _log("%s %s: generating" % (key, mat.name))
+        w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id, wide_groups=mat.wide_groups)
+        wg = gpu(w)
+        mats.append(q4.q4_quantize(wg))
+        del wg
+        rows = _sample_rows(mat.n, np.random.default_rng(mat.tensor_id), count=128)
+        samples.append((rows, orc.quantize(w[rows])))
+        del w
+    _log("%s: q4_gemv_multi over %d matrices" % (key, len(mats)))
+    ys = q4.q4_gemv_multi(xg, mats)
+    torch.cuda.synchronize()
+    for (mat, _), y, (p, s), (rows, (rp, rs)) in zip(wl.cases, ys, mats, samples):
+        assert torch.equal(y, q4.q4_gemv(xg, p, s)), mat.name
+        y_ref, bound = orc.matmul(x, rp, rs)
+        gy = y.cpu().numpy().astype(np.float64)[:, rows]
+        assert_within(gy, y_ref, bound, "%s %s" % (key, mat.name))
+
+
+# --------------------------------------------------------------------------
 # the five workload configurations at full size, compared on sampled rows
 # --------------------------------------------------------------------------
 
