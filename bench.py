@@ -22,7 +22,8 @@ roofline = the dominant kernel (the LM-head GEMV): its algorithmic bytes per
            stream around a batch of back-to-back launches over the rotated
            copies), against the 8 TB/s HBM3E peak
 detail   = the other halves of the hot path measured in the same run: the 4B
-           LM head (k = 2560), the M = 512 prefill GEMM (TFLOP/s against the
+           LM head (k = 2560), the 0.8B LM head in the fp16 weight format
+           (q4_gemv_f16, 2 bytes per weight), the M = 512 prefill GEMM (TFLOP/s against the
            2.5 PFLOP/s dense fp16 MFMA peak) and the quantizer (GB/s); --all
            adds the 4B decode set, the M = 8 verify LM head and the
            M = 16/128/2048 prefill GEMMs
@@ -370,6 +371,39 @@ def lm_head_rate(torch, q4, lib, mat, iters):
     return out
 
 
+def f16_gemv_rate(torch, q4, lib, mat, m, iters):
+    """Back-to-back q4_gemv_f16 launches over rotated fp16 weight copies."""
+    import q4_inputs as qi
+    x = torch.from_numpy(qi.activations(m, mat.k)).cuda()
+    w0 = torch.from_numpy(qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)).cuda().half()
+    copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 2)))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    y = torch.empty((m, mat.n), dtype=torch.float32, device=x.device)
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def go(i):
+        st = lib.q4_gemv_f16(x.data_ptr(), ws[i % copies].data_ptr(), y.data_ptr(), m, mat.n,
+                             mat.k, sh)
+        if st != 0:
+            raise RuntimeError("q4_gemv_f16 failed with status %d" % st)
+    for i in range(3):
+        go(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        go(i)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / iters / 1e3
+    nbytes = mat.n * mat.k * 2 + 2 * m * mat.k + 4 * m * mat.n
+    del ws, w0
+    torch.cuda.empty_cache()
+    return {"matrix": mat.name + ".f16", "m": m, "n": mat.n, "k": mat.k, "us": round(t * 1e6, 3),
+            "GB_s": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "copies": copies}
+
+
 def gemm_case(torch, q4, lib, mat, m, outliers, iters):
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
@@ -514,6 +548,8 @@ def main() -> int:
               "rotation_copies": ds["copies"]}
     log("LM head 4B")
     detail["lm_head_4b"] = lm_head_rate(torch, q4, lib, qi.DECODE_4B[-1], 100)
+    log("F16 GEMV LM head 0.8B")
+    detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
     log("prefill GEMM M=512")
     detail["gemm_m512"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
     log("quantize 0.8B LM head")
@@ -531,6 +567,8 @@ def main() -> int:
             detail["gemm_m%d" % m] = gemm_case(torch, q4, lib, mat, m, m != 2048, 50)
         log("verify LM head M=8")
         detail["verify_m8_lm_head"] = gemm_case(torch, q4, lib, qi.LM_HEAD_4B_WIDE, 8, False, 50)
+        log("F16 GEMV LM head 4B, M=8")
+        detail["f16_gemv_lm_head_4b_m8"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 30)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 2
+#define Q4_ABI_VERSION 3
 #define Q4_GROUP 32
 #define Q4_MULTI_MAX 8
 
@@ -130,6 +130,22 @@ q4_status q4_gemv(const uint16_t* x, const uint8_t* packed,
 q4_status q4_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
                         const uint8_t* const* packed, const uint16_t* const* scales,
                         float* const* y, const int64_t* n, void* stream);
+
+/*
+ * q4_gemv_f16 -- decode-time product with fp16 weights, the second weight
+ * format of the QORA engines (QORA-4B article, quantization section, format
+ * table: F16 beside Q4; QORA-LLM-0.8B model card, "AVX-512 SIMD
+ * Acceleration", F16 GEMV row).  y[i][r] = sum_t x[i][t] * w[r][t].
+ *   x       [in]  fp16 bits [m, k], device, 1 <= m <= 8
+ *   w       [in]  fp16 bits [n, k], device (one output feature per row)
+ *   y       [out] fp32 [m, n], device
+ * Shape and alignment rules as above (k % 32 == 0 here too; w 16-byte
+ * aligned like x); m outside 1..8 -> Q4_ERR_SHAPE.
+ * Accuracy: products of two fp16 values are exact in fp32; fp32
+ * accumulation; the bound |y - y_ref| <= 1e-3 * sum|x * w| + 1e-6 holds.
+ */
+q4_status q4_gemv_f16(const uint16_t* x, const uint16_t* w, float* y,
+                      int64_t m, int64_t n, int64_t k, void* stream);
 
 /*
  * q4_gemm -- prefill product, same arguments and semantics as q4_gemv, for

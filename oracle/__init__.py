@@ -55,6 +55,8 @@ class Oracle:
         lib.q4o_quantize.argtypes = [p, i64, i64, p, p]
         lib.q4o_quantize.restype = ctypes.c_int
         lib.q4o_matmul.argtypes = [p, p, p, i64, i64, i64, p, p]
+        lib.q4o_matmul_f16.argtypes = [p, p, i64, i64, i64, p, p]
+        lib.q4o_matmul_f16.restype = ctypes.c_int
         lib.q4o_matmul.restype = ctypes.c_int
         lib.q4o_threads.argtypes = []
         lib.q4o_threads.restype = ctypes.c_int
@@ -111,6 +113,29 @@ class Oracle:
                                  bound.ctypes.data)
         if st != OK:
             raise ValueError("oracle matmul failed with status %d" % st)
+        return y, bound
+
+
+    def matmul_f16(self, x_f16: np.ndarray, w_f16: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        """x binary16 [m,k], w binary16 [n,k] -> (y, bound) fp64 [m,n]."""
+        x = np.ascontiguousarray(x_f16)
+        w = np.ascontiguousarray(w_f16)
+        if x.dtype == np.float16:
+            x = x.view(np.uint16)
+        if w.dtype == np.float16:
+            w = w.view(np.uint16)
+        if x.dtype != np.uint16 or w.dtype != np.uint16 or x.ndim != 2 or w.ndim != 2:
+            raise ValueError("x and w must be 2-D binary16")
+        m, k = x.shape
+        n = w.shape[0]
+        if w.shape != (n, k):
+            raise ValueError("w must be [n, k]")
+        y = np.empty((m, n), dtype=np.float64)
+        bound = np.empty((m, n), dtype=np.float64)
+        st = self.lib.q4o_matmul_f16(x.ctypes.data, w.ctypes.data, m, n, k, y.ctypes.data,
+                                     bound.ctypes.data)
+        if st != OK:
+            raise ValueError("oracle matmul_f16 failed with status %d" % st)
         return y, bound
 
 

@@ -210,6 +210,47 @@ int q4o_matmul(const uint16_t* x, const uint8_t* packed,
     return Q4O_OK;
 }
 
+/* ---------------------------------------------------------------------- */
+/* Product with fp16 weights (the pages' other weight format)              */
+/* ---------------------------------------------------------------------- */
+
+/* QORA-4B forum article, quantization section (format table: F16 beside
+ * Q4) and QORA-LLM-0.8B model card, "AVX-512 SIMD Acceleration" (F16 GEMV
+ * row: each fp16 weight widened, then multiply-accumulated).  The plain
+ * definition y[i,r] = sum_t x[i,t] * w[r,t], in fp64: every product of two
+ * binary16 values is exact there. */
+int q4o_matmul_f16(const uint16_t* x, const uint16_t* w, int64_t m, int64_t n,
+                   int64_t k, double* y, double* bound) {
+    if (!x || !w || !y)
+        return Q4O_ERR_NULL;
+    if (m < 1 || n < 1 || k < 1)
+        return Q4O_ERR_SHAPE;
+    double* xd = (double*)malloc((size_t)(m * k) * sizeof(double));
+    if (!xd)
+        return Q4O_ERR_NOMEM;
+    for (int64_t i = 0; i < m * k; ++i)
+        xd[i] = q4o_f16_to_f64(x[i]);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        const uint16_t* row = w + r * k;
+        for (int64_t i = 0; i < m; ++i) {
+            const double* xrow = xd + i * k;
+            double sum = 0.0, sum_abs = 0.0;
+            for (int64_t t = 0; t < k; ++t) {
+                double prod = xrow[t] * q4o_f16_to_f64(row[t]);
+                sum += prod;
+                sum_abs += fabs(prod);
+            }
+            y[i * n + r] = sum;
+            if (bound)
+                bound[i * n + r] = sum_abs;
+        }
+    }
+    free(xd);
+    return Q4O_OK;
+}
+
 /* Number of threads the parallel loops above use (1 without OpenMP). */
 int q4o_threads(void) {
 #ifdef _OPENMP

@@ -30,6 +30,11 @@ int q4o_matmul(const uint16_t* x, const uint8_t* packed,
                const uint16_t* scales, int64_t m, int64_t n, int64_t k,
                double* y, double* bound);
 
+/* y[i,r] = sum_t x[i,t] * w[r,t] in fp64, bound[i,r] = sum_t |x[i,t] * w[r,t]|
+ * (may be NULL).  x binary16 bits [m,k], w binary16 bits [n,k]. */
+int q4o_matmul_f16(const uint16_t* x, const uint16_t* w, int64_t m, int64_t n,
+                   int64_t k, double* y, double* bound);
+
 /* Threads used by the parallel loops. */
 int q4o_threads(void);
 

@@ -10,6 +10,7 @@ Functions keep the C names:
   q4_gemv(x, packed, scales)           -> y fp32 [m,n]     (1 <= m <= 8)
   q4_gemm(x, packed, scales)           -> y fp32 [m,n]     (any m >= 1)
   q4_gemv_multi(x, [(packed, scales), ...]) -> [y_i fp32 [m,n_i]]  (shared x, <= 8 matrices)
+  q4_gemv_f16(x, w)                    -> y fp32 [m,n]     (fp16 weights, 1 <= m <= 8)
   q4_status_str(code), q4_abi_version()
 Outputs may be passed in (``out=``) to avoid allocation.
 """
@@ -23,7 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4.so")
 
 EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm",
-            "q4_gemv_multi")
+            "q4_gemv_multi", "q4_gemv_f16")
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE = range(6)
 GROUP = 32
 MULTI_MAX = 8
@@ -60,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.q4_gemv_multi.argtypes = [p, i64, i64, ctypes.c_int32, p, p, p, p, p]
     lib.q4_gemv_multi.restype = ctypes.c_int
+    lib.q4_gemv_f16.argtypes = [p, p, p, i64, i64, i64, p]
+    lib.q4_gemv_f16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -184,3 +187,25 @@ def q4_gemv_multi(x, mats, out=None, stream=None):
                                   _stream(stream, x.device))
     _check("q4_gemv_multi", st)
     return ys
+
+
+def q4_gemv_f16(x, w, out=None, stream=None):
+    """Decode product with fp16 weights: y[m, n] = x[m, k] . w[n, k]^T, 1 <= m <= 8."""
+    import torch
+    _require(x, torch.float16, "x")
+    _require(w, torch.float16, "w")
+    if x.dim() != 2 or w.dim() != 2 or w.shape[1] != x.shape[1]:
+        raise ValueError("x [m, k] and w [n, k] required, got %s and %s"
+                         % (tuple(x.shape), tuple(w.shape)))
+    m, k = x.shape
+    n = w.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+    if out is not None:
+        _require(y, torch.float32, "out")
+        if tuple(y.shape) != (m, n):
+            raise ValueError("out must be [m, n]")
+    with torch.cuda.device(x.device):
+        st = load().q4_gemv_f16(x.data_ptr(), w.data_ptr(), y.data_ptr(), m, n, k,
+                                _stream(stream, x.device))
+    _check("q4_gemv_f16", st)
+    return y

@@ -30,6 +30,10 @@ hipError_t launch_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int count,
                              const uint8_t* const* packed, const uint16_t* const* scales,
                              float* const* y, const int64_t* n, hipStream_t stream);
 
+// fp16 weights [n, k], 1 <= m <= 8.
+hipError_t launch_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
+                           int64_t n, int64_t k, hipStream_t stream);
+
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed,
                        const uint16_t* scales, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);

@@ -283,6 +283,61 @@ def errors(o):
     assert st == 0 and int(sc[1, 0]) == 0x7BFF
 
 
+# -- the product with fp16 weights -------------------------------------------
+
+def f16_product_vs_numpy(o):
+    rng = np.random.default_rng(31)
+    for (m, n, k) in [(1, 7, 96), (3, 5, 40), (8, 33, 128)]:
+        x = (rng.standard_normal((m, k)) * 3).astype(np.float16)
+        w = (rng.standard_normal((n, k)) * 0.05).astype(np.float16)
+        y, bound = o.matmul_f16(x, w)
+        xd, wd = x.astype(np.float64), w.astype(np.float64)
+        ref = xd @ wd.T
+        ref_bound = np.abs(xd) @ np.abs(wd).T
+        assert np.all(np.abs(y - ref) <= 1e-12 * ref_bound + 1e-300)
+        assert np.allclose(bound, ref_bound, rtol=1e-12, atol=0)
+
+
+def f16_product_exact(o):
+    rng = np.random.default_rng(33)
+    m, n, k = 2, 3, 24
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    w = (rng.standard_normal((n, k)) * 0.1).astype(np.float16)
+    y, bound = o.matmul_f16(x, w)
+    for i in range(m):
+        for r in range(n):
+            terms = [Fraction(float(x[i, t])) * Fraction(float(w[r, t])) for t in range(k)]
+            tot, tot_abs = sum(terms), sum(abs(t) for t in terms)
+            assert abs(Fraction(float(y[i, r])) - tot) <= tot_abs * Fraction(1, 2 ** 50)
+            assert abs(Fraction(float(bound[i, r])) - tot_abs) <= tot_abs * Fraction(1, 2 ** 50)
+
+
+def f16_product_special(o):
+    rng = np.random.default_rng(35)
+    n, k = 4, 40
+    w = rng.standard_normal((n, k)).astype(np.float16)
+    y, _ = o.matmul_f16(np.eye(k, dtype=np.float16), w)      # row e selects element e
+    assert np.array_equal(y, w.astype(np.float64).T)
+    y, b = o.matmul_f16(np.zeros((2, k), np.float16), w)
+    assert np.all(y == 0) and np.all(b == 0)
+    y, _ = o.matmul_f16(rng.standard_normal((2, k)).astype(np.float16), np.zeros((n, k), np.float16))
+    assert np.all(y == 0)
+    xp = np.abs(rng.standard_normal((1, k))).astype(np.float16)
+    y, b = o.matmul_f16(xp, np.abs(w))                        # all terms >= 0: bound == y
+    assert np.array_equal(y, b)
+    y, b = o.matmul_f16(xp, -np.abs(w))                       # all terms <= 0: bound == -y
+    assert np.array_equal(-y, b)
+
+
+def f16_errors(o):
+    st = o.lib.q4o_matmul_f16(None, None, 1, 1, 32, None, None)
+    assert st == 1
+    x = np.zeros((1, 8), np.uint16)
+    out = np.zeros((1, 1))
+    assert o.lib.q4o_matmul_f16(x.ctypes.data, x.ctypes.data, 1, 1, 0, out.ctypes.data, None) == 2
+
+
 ALL_PINS = [golden_groups, golden_product, f16_conversion, scale_vs_numpy,
             levels_brute_force, invariants, product_vs_numpy, product_exact,
-            product_special, errors]
+            product_special, errors, f16_product_vs_numpy, f16_product_exact,
+            f16_product_special, f16_errors]

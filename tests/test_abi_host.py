@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "q4.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q4_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
     import q4_group_quantized_amd as q4
     out = subprocess.run(["nm", "-D", "--defined-only", q4.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (q4_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (q4_[a-z0-9_]+)\b", out))
     missing = [f for f in declared_functions() if f not in exported]
     assert not missing, missing
     for f in declared_functions():
@@ -103,6 +103,23 @@ def test_gemv_rejects_more_than_eight_rows(lib):
     assert lib.q4_gemv(FAKE, FAKE, FAKE, FAKE, 9, 8, 64, None) == 2
 
 
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, FAKE, FAKE, 1, 8, 64), 1),
+    ((FAKE, NULL, FAKE, 1, 8, 64), 1),
+    ((FAKE, FAKE, NULL, 1, 8, 64), 1),
+    ((FAKE, FAKE, FAKE, 0, 8, 64), 2),
+    ((FAKE, FAKE, FAKE, 9, 8, 64), 2),
+    ((FAKE, FAKE, FAKE, 1, 0, 64), 2),
+    ((FAKE, FAKE, FAKE, 1, 8, 48), 2),
+    ((FAKE, FAKE, FAKE, 1, 8, 16), 2),
+    ((FAKE + 2, FAKE, FAKE, 1, 8, 64), 3),
+    ((FAKE, FAKE + 8, FAKE, 1, 8, 64), 3),
+    ((FAKE, FAKE, FAKE + 2, 1, 8, 64), 3),
+])
+def test_gemv_f16_rejects_bad_arguments(lib, args, expect):
+    assert lib.q4_gemv_f16(*args, None) == expect
+
+
 def _multi(lib, x, m, k, packed, scales, y, n, count=None):
     """Call q4_gemv_multi with host arrays built from Python lists (None = NULL array)."""
     def arr(vals, ctype):
@@ -144,7 +161,7 @@ def test_gemv_multi_rejects_bad_arguments(lib, case, expect):
 
 def test_binding_names_match_the_c_abi():
     import q4_group_quantized_amd as q4
-    for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_gemv_multi", "q4_status_str",
-                 "q4_abi_version"):
+    for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_gemv_multi", "q4_gemv_f16",
+                 "q4_status_str", "q4_abi_version"):
         assert callable(getattr(q4, name))
     assert set(q4.EXPORTED) == set(declared_functions())

@@ -40,6 +40,14 @@ MUTANTS = [
      "for (int t = 0; t < 31; ++t) {\n                    int64_t kk"),
     ("bound_not_absolute", "acc_abs += fabs(s) * dot_abs;", "acc_abs += fabs(s * dot);"),
     ("output_index", "y[i * n + r] = acc;", "y[r * m + i] = acc;"),
+    ("f16_sign", "double prod = xrow[t] *", "double prod = -xrow[t] *"),
+    ("f16_weight_index", "const uint16_t* row = w + r * k;", "const uint16_t* row = w + r;"),
+    ("f16_dropped_term", "for (int64_t t = 0; t < k; ++t) {\n                double prod",
+     "for (int64_t t = 1; t < k; ++t) {\n                double prod"),
+    ("f16_bound_not_absolute", "sum_abs += fabs(prod);", "sum_abs += prod;"),
+    ("f16_output_index", "y[i * n + r] = sum;", "y[r * m + i] = sum;"),
+    ("f16_widened_as_zero_exponent", "double prod = xrow[t] * q4o_f16_to_f64(row[t]);",
+     "double prod = xrow[t] * (double)row[t];"),
 ]
 
 

@@ -289,6 +289,78 @@ def test_gemv_multi_decode_set_full_size(q4, orc, key):
 
 
 # --------------------------------------------------------------------------
+# fp16 weights (q4_gemv_f16)
+# --------------------------------------------------------------------------
+
+F16_SHAPES = [(1, 32), (15, 64), (17, 96), (33, 256), (100, 1056), (257, 2560), (1024, 1024),
+              (5, 8192), (61, 4096), (4099, 128)]
+
+
+def _f16_case(m, n, k, seed):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.05).astype(np.float16)
+    x = (rng.standard_normal((m, k)) * 2).astype(np.float16)
+    return x, w
+
+
+@pytest.mark.parametrize("n,k", F16_SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 5, 8])
+def test_gemv_f16_product(q4, orc, m, n, k):
+    x, w = _f16_case(m, n, k, seed=m * 7 + n + k)
+    _log("q4_gemv_f16 m=%d n=%d k=%d" % (m, n, k))
+    y = q4.q4_gemv_f16(gpu(x), gpu(w))
+    torch.cuda.synchronize()
+    y_ref, bound = orc.matmul_f16(x, w)
+    assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound,
+                  "q4_gemv_f16 m=%d n=%d k=%d" % (m, n, k))
+
+
+def test_gemv_f16_exact_special_inputs(q4):
+    rng = np.random.default_rng(78)
+    n, k = 37, 96
+    w = rng.standard_normal((n, k)).astype(np.float16)
+    wg = gpu(w)
+    _log("q4_gemv_f16 one-hot / zero inputs")
+    for e0 in range(0, k, 8):
+        x = np.eye(k, dtype=np.float16)[e0:e0 + 8]
+        y = q4.q4_gemv_f16(gpu(x), wg).cpu().numpy().astype(np.float64)
+        assert np.array_equal(y, w.astype(np.float64).T[e0:e0 + 8]), "one-hot rows %d.." % e0
+    y = q4.q4_gemv_f16(gpu(np.zeros((3, k), np.float16)), wg)
+    assert bool(torch.all(y == 0))
+    y = q4.q4_gemv_f16(gpu(rng.standard_normal((2, k)).astype(np.float16)),
+                       gpu(np.zeros((n, k), np.float16)))
+    assert bool(torch.all(y == 0))
+
+
+def test_gemv_f16_deterministic_and_binding_errors(q4):
+    x, w = _f16_case(8, 999, 2560, seed=6)
+    xg, wg = gpu(x), gpu(w)
+    a = q4.q4_gemv_f16(xg, wg)
+    b = q4.q4_gemv_f16(xg, wg)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv_f16(gpu(np.zeros((9, 64), np.float16)), gpu(np.zeros((4, 64), np.float16)))
+    with pytest.raises(ValueError):
+        q4.q4_gemv_f16(gpu(np.zeros((1, 64), np.float16)), gpu(np.zeros((4, 32), np.float16)))
+
+
+@pytest.mark.parametrize("mat,m", [(qi.DECODE_08B[-1], 1), (qi.DECODE_4B[-1], 8)],
+                         ids=["lm_head_08b-m1", "lm_head_4b-m8"])
+def test_gemv_f16_lm_head_full_size(q4, orc, mat, m):
+    """The LM head in the fp16 format at full size: sampled rows against the oracle."""
+    _log("f16 %s m=%d n=%d k=%d: generating" % (mat.name, m, mat.n, mat.k))
+    w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id).astype(np.float16)
+    x = qi.activations(m, mat.k)
+    y = q4.q4_gemv_f16(gpu(x), gpu(w))
+    torch.cuda.synchronize()
+    rows = _sample_rows(mat.n, np.random.default_rng(mat.tensor_id))
+    y_ref, bound = orc.matmul_f16(x, w[rows])
+    gy = y.cpu().numpy().astype(np.float64)[:, rows]
+    assert_within(gy, y_ref, bound, "f16 %s" % mat.name)
+
+
+# --------------------------------------------------------------------------
 # the five workload configurations at full size, compared on sampled rows
 # --------------------------------------------------------------------------
 
