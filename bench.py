@@ -22,8 +22,10 @@ roofline = the dominant kernel (the LM-head GEMV): its algorithmic bytes per
            stream around a batch of back-to-back launches over the rotated
            copies), against the 8 TB/s HBM3E peak
 detail   = the other halves of the hot path measured in the same run: the 4B
-           LM head (k = 2560), the 0.8B LM head in the fp16 weight format
-           (q4_gemv_f16, 2 bytes per weight), the M = 512 prefill GEMM (TFLOP/s against the
+           LM head (k = 2560), the 0.8B LM head with its top-20 epilogue
+           (q4_gemv_topk, against q4_gemv + torch.topk), the 0.8B LM head in
+           the fp16 weight format (q4_gemv_f16, 2 bytes per weight), the
+           M = 512 prefill GEMM (TFLOP/s against the
            2.5 PFLOP/s dense fp16 MFMA peak) and the quantizer (GB/s); --all
            adds the 4B decode set, the M = 8 verify LM head and the
            M = 16/128/2048 prefill GEMMs
@@ -404,6 +406,51 @@ def f16_gemv_rate(torch, q4, lib, mat, m, iters):
             "copies": copies}
 
 
+def topk_rate(torch, q4, lib, mat, m, topk, iters):
+    """q4_gemv_topk on an LM head (rotated weights) against q4_gemv followed by
+    torch.topk on the logits."""
+    import q4_inputs as qi
+    x = torch.from_numpy(qi.activations(m, mat.k)).cuda()
+    copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 9 // 16)))
+    p = Product(torch, q4, mat, m, x, copies)
+    sh = torch.cuda.current_stream().cuda_stream
+    need = q4.q4_gemv_topk_workspace_size(m, mat.n, mat.k)
+    ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    values = torch.empty((m, topk), dtype=torch.float32, device=x.device)
+    rows = torch.empty((m, topk), dtype=torch.int32, device=x.device)
+
+    def fused(i):
+        pk, sc = p.copies[i % copies]
+        st = lib.q4_gemv_topk(x.data_ptr(), pk.data_ptr(), sc.data_ptr(), m, mat.n, mat.k, topk,
+                              values.data_ptr(), rows.data_ptr(), ws.data_ptr(), need, sh)
+        if st != 0:
+            raise RuntimeError("q4_gemv_topk failed with status %d" % st)
+
+    def separate(i):
+        launch(lib, "q4_gemv", p.args(i), sh)
+        torch.topk(p.y, topk, dim=1)
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(iters):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters / 1e3
+    t_fused, t_sep = timed(fused), timed(separate)
+    out = {"matrix": mat.name, "m": m, "topk": topk, "us_fused": round(t_fused * 1e6, 3),
+           "us_gemv_then_torch_topk": round(t_sep * 1e6, 3),
+           "GB_s_fused": round(p.bytes / t_fused / 1e9, 1),
+           "hbm_frac_fused": round(p.bytes / t_fused / 1e9 / HBM_PEAK_GBS, 4)}
+    del p, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def gemm_case(torch, q4, lib, mat, m, outliers, iters):
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
@@ -548,6 +595,8 @@ def main() -> int:
               "rotation_copies": ds["copies"]}
     log("LM head 4B")
     detail["lm_head_4b"] = lm_head_rate(torch, q4, lib, qi.DECODE_4B[-1], 100)
+    log("LM head 0.8B with top-20 epilogue")
+    detail["lm_head_topk20_08b"] = topk_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 20, 100)
     log("F16 GEMV LM head 0.8B")
     detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
     log("prefill GEMM M=512")
@@ -567,6 +616,8 @@ def main() -> int:
             detail["gemm_m%d" % m] = gemm_case(torch, q4, lib, mat, m, m != 2048, 50)
         log("verify LM head M=8")
         detail["verify_m8_lm_head"] = gemm_case(torch, q4, lib, qi.LM_HEAD_4B_WIDE, 8, False, 50)
+        log("verify LM head M=8 with argmax epilogue")
+        detail["lm_head_argmax_4b_m8"] = topk_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 1, 30)
         log("F16 GEMV LM head 4B, M=8")
         detail["f16_gemv_lm_head_4b_m8"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 30)
 

@@ -31,8 +31,8 @@
  *
  * Common argument rules for every entry point:
  *   - Pointers are DEVICE pointers owned by the caller.  The library never
- *     allocates, frees or keeps them after the call returns, and uses no
- *     workspace.
+ *     allocates, frees or keeps them after the call returns.  Only
+ *     q4_gemv_topk takes a workspace, which the caller provides.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *     Work is enqueued asynchronously; the caller keeps inputs alive and
  *     unmodified until the stream has completed it.  Outputs are overwritten
@@ -51,15 +51,17 @@
 #ifndef Q4_H
 #define Q4_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 3
+#define Q4_ABI_VERSION 4
 #define Q4_GROUP 32
 #define Q4_MULTI_MAX 8
+#define Q4_TOPK_MAX 32
 
 typedef enum {
     Q4_OK = 0,
@@ -67,7 +69,8 @@ typedef enum {
     Q4_ERR_SHAPE = 2,   /* m, n or k outside the documented ranges            */
     Q4_ERR_ALIGN = 3,   /* a pointer breaks the alignment rule                */
     Q4_ERR_LAUNCH = 4,  /* the HIP runtime refused or failed the launch       */
-    Q4_ERR_DEVICE = 5   /* no usable gfx950 device is current                 */
+    Q4_ERR_DEVICE = 5,  /* no usable gfx950 device is current                 */
+    Q4_ERR_WORKSPACE = 6 /* workspace NULL, smaller than required or not 256-B aligned */
 } q4_status;
 
 /* Version of this interface; equals Q4_ABI_VERSION of the built library. */
@@ -146,6 +149,34 @@ q4_status q4_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
  */
 q4_status q4_gemv_f16(const uint16_t* x, const uint16_t* w, float* y,
                       int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * q4_gemv_topk -- the LM-head product followed by its decoding epilogue: for
+ * every token the topk largest logits y[i][r] (r < n) and their rows, without
+ * returning the logits.  Greedy decoding takes topk = 1; top-k sampling keeps
+ * the k best candidates (QORA-LLM-0.8B model card, CLI options and "Sampling
+ * Defaults", top_k = 20); m up to 8 covers the verify batch of speculative
+ * decoding (Rai article, speculative decoding section).  The logits are those
+ * q4_gemv computes, bit for bit.
+ *   x, packed, scales, m, n, k: as q4_gemv (1 <= m <= 8, n <= 2^31 - 2)
+ *   topk          1 .. min(Q4_TOPK_MAX, n)
+ *   values  [out] fp32 [m, topk], device: largest first
+ *   rows    [out] int32 [m, topk], device: the row (vocabulary id) of each
+ *   workspace     device scratch of at least q4_gemv_topk_workspace_size(m,
+ *                 n, k) bytes, 256-byte aligned, caller-owned; its contents
+ *                 are overwritten; calls that share one workspace must not
+ *                 overlap in time
+ * Order: by value, larger first; equal values by row, smaller first (+0 ranks
+ * above -0).  NaN logits rank below every number; a slot that no number
+ * fills reports NaN and row -1.  Deterministic.
+ * Errors: as q4_gemv; topk out of range -> Q4_ERR_SHAPE; workspace NULL, too
+ * small or misaligned -> Q4_ERR_WORKSPACE.
+ */
+size_t q4_gemv_topk_workspace_size(int64_t m, int64_t n, int64_t k);
+q4_status q4_gemv_topk(const uint16_t* x, const uint8_t* packed,
+                       const uint16_t* scales, int64_t m, int64_t n, int64_t k,
+                       int32_t topk, float* values, int32_t* rows,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * q4_gemm -- prefill product, same arguments and semantics as q4_gemv, for

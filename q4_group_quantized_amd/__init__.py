@@ -11,6 +11,8 @@ Functions keep the C names:
   q4_gemm(x, packed, scales)           -> y fp32 [m,n]     (any m >= 1)
   q4_gemv_multi(x, [(packed, scales), ...]) -> [y_i fp32 [m,n_i]]  (shared x, <= 8 matrices)
   q4_gemv_f16(x, w)                    -> y fp32 [m,n]     (fp16 weights, 1 <= m <= 8)
+  q4_gemv_topk(x, packed, scales, topk) -> (values fp32 [m,topk], rows int32 [m,topk])
+  q4_gemv_topk_workspace_size(m, n, k) -> bytes of device workspace q4_gemv_topk needs
   q4_status_str(code), q4_abi_version()
 Outputs may be passed in (``out=``) to avoid allocation.
 """
@@ -24,8 +26,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4.so")
 
 EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm",
-            "q4_gemv_multi", "q4_gemv_f16")
-Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE = range(6)
+            "q4_gemv_multi", "q4_gemv_f16", "q4_gemv_topk", "q4_gemv_topk_workspace_size")
+(Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE,
+ Q4_ERR_WORKSPACE) = range(7)
+TOPK_MAX = 32
 GROUP = 32
 MULTI_MAX = 8
 
@@ -63,6 +67,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q4_gemv_multi.restype = ctypes.c_int
     lib.q4_gemv_f16.argtypes = [p, p, p, i64, i64, i64, p]
     lib.q4_gemv_f16.restype = ctypes.c_int
+    lib.q4_gemv_topk_workspace_size.argtypes = [i64, i64, i64]
+    lib.q4_gemv_topk_workspace_size.restype = ctypes.c_size_t
+    lib.q4_gemv_topk.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int32, p, p, p,
+                                 ctypes.c_size_t, p]
+    lib.q4_gemv_topk.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -209,3 +218,45 @@ def q4_gemv_f16(x, w, out=None, stream=None):
                                 _stream(stream, x.device))
     _check("q4_gemv_f16", st)
     return y
+
+
+def q4_gemv_topk_workspace_size(m: int, n: int, k: int) -> int:
+    """Bytes of device workspace q4_gemv_topk needs on the current device (0: invalid)."""
+    return int(load().q4_gemv_topk_workspace_size(m, n, k))
+
+
+def q4_gemv_topk(x, packed, scales, topk, workspace=None, out=None, stream=None):
+    """The topk largest logits of x . dequant(W)^T per token and their rows.
+
+    Returns (values fp32 [m, topk], rows int32 [m, topk]), largest first, equal
+    values by smaller row.  `workspace` (uint8 device tensor) is allocated when
+    not given; `out` may pass the (values, rows) tensors."""
+    import torch
+    _require(x, torch.float16, "x")
+    _require(packed, torch.uint8, "packed")
+    _require(scales, torch.float16, "scales")
+    m, k = x.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 2 != k or tuple(scales.shape) != (n, k // GROUP):
+        raise ValueError("shapes disagree: x %s packed %s scales %s"
+                         % (tuple(x.shape), tuple(packed.shape), tuple(scales.shape)))
+    with torch.cuda.device(x.device):
+        need = q4_gemv_topk_workspace_size(m, n, k)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1) + 256, dtype=torch.uint8, device=x.device)
+        _require(workspace, torch.uint8, "workspace")
+        ws_ptr = workspace.data_ptr()
+        pad = (-ws_ptr) % 256
+        ws_bytes = workspace.numel() - pad if workspace.numel() >= pad else 0
+        if out is None:
+            values = torch.empty((m, topk), dtype=torch.float32, device=x.device)
+            rows = torch.empty((m, topk), dtype=torch.int32, device=x.device)
+        else:
+            values, rows = out
+            _require(values, torch.float32, "values")
+            _require(rows, torch.int32, "rows")
+        st = load().q4_gemv_topk(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), m, n, k,
+                                 int(topk), values.data_ptr(), rows.data_ptr(), ws_ptr + pad,
+                                 ws_bytes, _stream(stream, x.device))
+    _check("q4_gemv_topk", st)
+    return values, rows

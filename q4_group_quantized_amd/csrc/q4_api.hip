@@ -94,6 +94,7 @@ const char* q4_status_str(q4_status status) {
         case Q4_ERR_ALIGN: return "misaligned pointer (x, packed, w: 16 B; scales: 2 B; y: 4 B)";
         case Q4_ERR_LAUNCH: return "kernel launch failed";
         case Q4_ERR_DEVICE: return "current device is not a usable gfx950";
+        case Q4_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     }
     return "unknown status";
 }
@@ -142,6 +143,34 @@ q4_status q4_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
     if ((st = device_ok()) != Q4_OK) return st;
     return map_launch(q4::launch_gemv_f16(x, w, y, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
+size_t q4_gemv_topk_workspace_size(int64_t m, int64_t n, int64_t k) {
+    if (check_nk(n, k) != Q4_OK || m < 1 || m > 8) return 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || !q4::device_usable(dev))
+        return 0;
+    return q4::gemv_topk_workspace(m, n, k, q4::device_info(dev).cu_count);
+}
+
+q4_status q4_gemv_topk(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
+                       int64_t m, int64_t n, int64_t k, int32_t topk, float* values,
+                       int32_t* rows, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !packed || !scales || !values || !rows) return Q4_ERR_NULL;
+    q4_status st = check_nk(n, k);
+    if (st != Q4_OK) return st;
+    if (m < 1 || m > 8 || topk < 1 || topk > Q4_TOPK_MAX || topk > n || n > 0x7FFFFFFE)
+        return Q4_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(values, 4) ||
+        !aligned(rows, 4))
+        return Q4_ERR_ALIGN;
+    if ((st = device_ok()) != Q4_OK) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return Q4_ERR_DEVICE;
+    const size_t need = q4::gemv_topk_workspace(m, n, k, q4::device_info(dev).cu_count);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4_ERR_WORKSPACE;
+    return map_launch(q4::launch_gemv_topk(x, packed, scales, m, n, k, topk, values, rows,
+                                           workspace, static_cast<hipStream_t>(stream)));
 }
 
 q4_status q4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* scales, float* y,

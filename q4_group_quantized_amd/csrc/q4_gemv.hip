@@ -46,6 +46,7 @@
 #include "q4.h"
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
+#include "q4_topk.hpp"
 
 namespace q4 {
 namespace {
@@ -380,9 +381,16 @@ static_assert(kGemv1MaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MUL
 // (this wave's own rows, still cached), so every load is unconditional and
 // the compiler keeps PF steps outstanding instead of draining the queue; the
 // last PF steps are computed after the loop without new loads.
-template <int LPR, int GPL, int PF>
+//
+// TOPK: instead of storing y, every wave keeps the 32 largest (logit, row)
+// keys of its rows (q4_topk.hpp): each step's RPS results go to a 64-entry
+// wave buffer in LDS, merged into the running list whenever it is full; at
+// the end the four lists of a workgroup are merged and written to
+// partials[blockIdx.x * 32 .. +32) (idle waves contribute empty lists).
+template <int LPR, int GPL, int PF, bool TOPK>
 __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
-    const uint16_t* __restrict__ x, int K, Gemv1Segments seg, SpliceConsts kc) {
+    const uint16_t* __restrict__ x, int K, Gemv1Segments seg, SpliceConsts kc,
+    uint64_t* __restrict__ partials) {
     constexpr int RPS = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int sub = lane % LPR;
@@ -406,10 +414,34 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
         }
     }
     const int64_t lw = w - wave0;
-    if (lw >= waves) return;
+    const bool active = lw < waves;
+    if (!TOPK && !active) return;           // the top-k variant's idle waves join the final merge
     const int64_t q0 = lw * base + (lw < extra ? lw : extra);
-    const int64_t cnt = base + (lw < extra ? 1 : 0);
+    const int64_t cnt = active ? base + (lw < extra ? 1 : 0) : 0;
     const int64_t row0 = RPS * q0 + r;
+
+    // top-k state: running list (lanes 0..31) and this wave's candidate buffer
+    __shared__ uint64_t cand[TOPK ? kGemvWaves : 1][64];
+    uint64_t* buf = cand[TOPK ? (threadIdx.x >> 6) : 0];
+    uint64_t list = 0;
+    int filled = 0;                                   // steps in the buffer
+    auto flush = [&]() {
+        __builtin_amdgcn_wave_barrier();
+        const uint64_t key = lane < filled * RPS ? buf[lane] : 0;
+        __builtin_amdgcn_wave_barrier();
+        list = topk_merge_batch(list, key, lane);
+        filled = 0;
+    };
+    // result of step f for this lane's row: stored, or offered to the list
+    auto emit = [&](float acc, int64_t f) {
+        const int64_t row = row0 + RPS * f;
+        if (TOPK) {
+            if (sub == 0) buf[filled * RPS + r] = row < N ? topk_key(acc, (uint32_t)row) : 0;
+            if (++filled == 64 / RPS) flush();
+        } else {
+            if (sub == 0 && row < N) y[row] = acc;
+        }
+    };
 
     u32x4_t rp[PF][GPL];
     uint32_t rs[PF][GPL];
@@ -425,8 +457,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
             rs[slot][i] = sp[LPR * i];
         }
     };
+    if (cnt > 0) {
 #pragma unroll
-    for (int p = 0; p < PF; ++p) load(p, p);
+        for (int p = 0; p < PF; ++p) load(p, p);
+    }
 
     // this lane's activations, as fp16 pairs in unpack order
     uint32_t xr[GPL][16];
@@ -468,16 +502,28 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
         for (int p = 0; p < PF; ++p) {
             const float acc = compute(p);
             load(p, f0 + p + PF);
-            const int64_t row = row0 + RPS * (f0 + p);
-            if (sub == 0 && row < N) y[row] = acc;
+            emit(acc, f0 + p);
         }
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         if (f0 + p < cnt) {
             const float acc = compute(p);
-            const int64_t row = row0 + RPS * (f0 + p);
-            if (sub == 0 && row < N) y[row] = acc;
+            emit(acc, f0 + p);
+        }
+    }
+    if constexpr (TOPK) {
+        // the workgroup's four lists -> one, in partials[blockIdx.x * 32 ..)
+        if (filled > 0) flush();
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (lane < kTopkList) cand[wave][lane] = list;
+        __syncthreads();
+        if (wave == 0) {
+            const uint64_t b1 = lane < kTopkList ? cand[1][lane] : cand[2][lane - kTopkList];
+            list = topk_merge_batch(list, b1, lane);
+            const uint64_t b2 = lane < kTopkList ? cand[3][lane] : 0;
+            list = topk_merge_batch(list, b2, lane);
+            if (lane < kTopkList) partials[(int64_t)blockIdx.x * kTopkList + lane] = list;
         }
     }
 }
@@ -492,7 +538,7 @@ constexpr int gemv1_prefetch(int gpl) {
 template <int LPR, int GPL>
 hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* const* packed,
                           const uint16_t* const* scales, float* const* y, const int64_t* n,
-                          hipStream_t stream) {
+                          uint64_t* partials, hipStream_t stream) {
     constexpr int PF = gemv1_prefetch(GPL);
     constexpr int RPS = 64 / LPR;
     int dev = 0;
@@ -519,24 +565,28 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
         wave0 += waves;
     }
     const int blocks = (int)((wave0 + kGemvWaves - 1) / kGemvWaves);
-    hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF>), dim3(blocks), dim3(kGemvThreads), 0, stream,
-                       x, k, seg, kSpliceConsts);
+    if (partials)
+        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, true>), dim3(blocks), dim3(kGemvThreads),
+                           0, stream, x, k, seg, kSpliceConsts, partials);
+    else
+        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, false>), dim3(blocks), dim3(kGemvThreads),
+                           0, stream, x, k, seg, kSpliceConsts, partials);
     return hipGetLastError();
 }
 
 template <int LPR>
 hipError_t launch_gemv1_lpr(const uint16_t* x, int k, int count, const uint8_t* const* packed,
                             const uint16_t* const* scales, float* const* y, const int64_t* n,
-                            hipStream_t stream) {
+                            uint64_t* partials, hipStream_t stream) {
     switch ((k / 32) / LPR) {
-        case 1: return launch_gemv1_t<LPR, 1>(x, k, count, packed, scales, y, n, stream);
-        case 2: return launch_gemv1_t<LPR, 2>(x, k, count, packed, scales, y, n, stream);
-        case 3: return launch_gemv1_t<LPR, 3>(x, k, count, packed, scales, y, n, stream);
-        case 4: return launch_gemv1_t<LPR, 4>(x, k, count, packed, scales, y, n, stream);
-        case 5: return launch_gemv1_t<LPR, 5>(x, k, count, packed, scales, y, n, stream);
-        case 6: return launch_gemv1_t<LPR, 6>(x, k, count, packed, scales, y, n, stream);
-        case 7: return launch_gemv1_t<LPR, 7>(x, k, count, packed, scales, y, n, stream);
-        default: return launch_gemv1_t<LPR, 8>(x, k, count, packed, scales, y, n, stream);
+        case 1: return launch_gemv1_t<LPR, 1>(x, k, count, packed, scales, y, n, partials, stream);
+        case 2: return launch_gemv1_t<LPR, 2>(x, k, count, packed, scales, y, n, partials, stream);
+        case 3: return launch_gemv1_t<LPR, 3>(x, k, count, packed, scales, y, n, partials, stream);
+        case 4: return launch_gemv1_t<LPR, 4>(x, k, count, packed, scales, y, n, partials, stream);
+        case 5: return launch_gemv1_t<LPR, 5>(x, k, count, packed, scales, y, n, partials, stream);
+        case 6: return launch_gemv1_t<LPR, 6>(x, k, count, packed, scales, y, n, partials, stream);
+        case 7: return launch_gemv1_t<LPR, 7>(x, k, count, packed, scales, y, n, partials, stream);
+        default: return launch_gemv1_t<LPR, 8>(x, k, count, packed, scales, y, n, partials, stream);
     }
 }
 
@@ -551,11 +601,11 @@ int gemv1_lanes_per_row(int64_t k) {
 
 hipError_t launch_gemv1(const uint16_t* x, int k, int count, const uint8_t* const* packed,
                         const uint16_t* const* scales, float* const* y, const int64_t* n,
-                        hipStream_t stream) {
+                        uint64_t* partials, hipStream_t stream) {
     switch (gemv1_lanes_per_row(k)) {
-        case 8: return launch_gemv1_lpr<8>(x, k, count, packed, scales, y, n, stream);
-        case 16: return launch_gemv1_lpr<16>(x, k, count, packed, scales, y, n, stream);
-        default: return launch_gemv1_lpr<32>(x, k, count, packed, scales, y, n, stream);
+        case 8: return launch_gemv1_lpr<8>(x, k, count, packed, scales, y, n, partials, stream);
+        case 16: return launch_gemv1_lpr<16>(x, k, count, packed, scales, y, n, partials, stream);
+        default: return launch_gemv1_lpr<32>(x, k, count, packed, scales, y, n, partials, stream);
     }
 }
 
@@ -576,15 +626,33 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed,
                        const uint16_t* scales, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
     if (m == 1 && gemv1_lanes_per_row(k) != 0)
-        return launch_gemv1(x, (int)k, 1, &packed, &scales, &y, &n, stream);
+        return launch_gemv1(x, (int)k, 1, &packed, &scales, &y, &n, nullptr, stream);
     return launch_gemv_blockdiag(x, packed, scales, y, m, n, k, stream);
+}
+
+int64_t gemv1_topk_lists(int64_t n, int64_t k, int cu_count) {
+    if (gemv1_lanes_per_row(k) == 0) return 0;
+    // the m = 1 launcher's grid for one matrix of n rows: at most one wave per
+    // SIMD, rounded up to whole workgroups
+    const int lpr = gemv1_lanes_per_row(k);
+    const int64_t rq = (n + 64 / lpr - 1) / (64 / lpr);
+    const int64_t max_waves = (int64_t)cu_count * kGemvWaves;
+    const int64_t per = (rq + max_waves - 1) / max_waves;
+    const int64_t waves = (rq + per - 1) / per;
+    return (waves + kGemvWaves - 1) / kGemvWaves;            // one list per workgroup
+}
+
+hipError_t launch_gemv1_topk(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
+                             int64_t n, int64_t k, uint64_t* partials, hipStream_t stream) {
+    float* none = nullptr;
+    return launch_gemv1(x, (int)k, 1, &packed, &scales, &none, &n, partials, stream);
 }
 
 hipError_t launch_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int count,
                              const uint8_t* const* packed, const uint16_t* const* scales,
                              float* const* y, const int64_t* n, hipStream_t stream) {
     if (m == 1 && gemv1_lanes_per_row(k) != 0)
-        return launch_gemv1(x, (int)k, count, packed, scales, y, n, stream);
+        return launch_gemv1(x, (int)k, count, packed, scales, y, n, nullptr, stream);
     for (int s = 0; s < count; ++s) {
         const hipError_t e = launch_gemv_blockdiag(x, packed[s], scales[s], y[s], m, n[s], k, stream);
         if (e != hipSuccess) return e;

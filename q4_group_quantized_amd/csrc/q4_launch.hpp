@@ -34,6 +34,18 @@ hipError_t launch_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int count,
 hipError_t launch_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
                            int64_t n, int64_t k, hipStream_t stream);
 
+// Lists of the fused m = 1 top-k GEMV for n rows (0 when k does not fit the
+// streaming kernel), and its launch writing those lists to `partials`.
+int64_t gemv1_topk_lists(int64_t n, int64_t k, int cu_count);
+hipError_t launch_gemv1_topk(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
+                             int64_t n, int64_t k, uint64_t* partials, hipStream_t stream);
+
+// LM-head product followed by the per-token top-k (1 <= topk <= 32).
+size_t gemv_topk_workspace(int64_t m, int64_t n, int64_t k, int cu_count);
+hipError_t launch_gemv_topk(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
+                            int64_t m, int64_t n, int64_t k, int topk, float* values,
+                            int32_t* rows, void* workspace, hipStream_t stream);
+
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed,
                        const uint16_t* scales, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);

@@ -50,7 +50,7 @@ def test_version_and_status_strings(lib):
     m = re.search(r"#define Q4_ABI_VERSION (\d+)", open(HEADER).read())
     assert lib.q4_abi_version() == int(m.group(1))
     seen = set()
-    for code in range(6):
+    for code in range(7):
         s = lib.q4_status_str(code).decode()
         assert s and s not in seen
         seen.add(s)
@@ -120,6 +120,31 @@ def test_gemv_f16_rejects_bad_arguments(lib, args, expect):
     assert lib.q4_gemv_f16(*args, None) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, FAKE, FAKE, 1, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 1),
+    ((FAKE, NULL, FAKE, 1, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 1),
+    ((FAKE, FAKE, NULL, 1, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 1),
+    ((FAKE, FAKE, FAKE, 1, 64, 64, 5, NULL, FAKE, FAKE, 1 << 20), 1),
+    ((FAKE, FAKE, FAKE, 1, 64, 64, 5, FAKE, NULL, FAKE, 1 << 20), 1),
+    ((FAKE, FAKE, FAKE, 0, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 2),
+    ((FAKE, FAKE, FAKE, 9, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 2),
+    ((FAKE, FAKE, FAKE, 1, 64, 64, 0, FAKE, FAKE, FAKE, 1 << 20), 2),
+    ((FAKE, FAKE, FAKE, 1, 64, 64, 33, FAKE, FAKE, FAKE, 1 << 20), 2),
+    ((FAKE, FAKE, FAKE, 1, 4, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 2),
+    ((FAKE, FAKE, FAKE, 1, 64, 48, 5, FAKE, FAKE, FAKE, 1 << 20), 2),
+    ((FAKE + 2, FAKE, FAKE, 1, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 3),
+    ((FAKE, FAKE, FAKE, 1, 64, 64, 5, FAKE + 2, FAKE, FAKE, 1 << 20), 3),
+    ((FAKE, FAKE, FAKE, 1, 64, 64, 5, FAKE, FAKE + 1, FAKE, 1 << 20), 3),
+])
+def test_gemv_topk_rejects_bad_arguments(lib, args, expect):
+    # argument checks run before the device check, so a GPU-less host sees them
+    assert lib.q4_gemv_topk(*args, None) == expect
+
+
+def test_gemv_topk_workspace_size_without_device(lib):
+    assert lib.q4_gemv_topk_workspace_size(1, 64, 48) == 0      # invalid shape
+
+
 def _multi(lib, x, m, k, packed, scales, y, n, count=None):
     """Call q4_gemv_multi with host arrays built from Python lists (None = NULL array)."""
     def arr(vals, ctype):
@@ -162,6 +187,7 @@ def test_gemv_multi_rejects_bad_arguments(lib, case, expect):
 def test_binding_names_match_the_c_abi():
     import q4_group_quantized_amd as q4
     for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_gemv_multi", "q4_gemv_f16",
-                 "q4_status_str", "q4_abi_version"):
+                 "q4_gemv_topk", "q4_gemv_topk_workspace_size", "q4_status_str",
+                 "q4_abi_version"):
         assert callable(getattr(q4, name))
     assert set(q4.EXPORTED) == set(declared_functions())

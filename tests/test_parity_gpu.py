@@ -289,6 +289,103 @@ def test_gemv_multi_decode_set_full_size(q4, orc, key):
 
 
 # --------------------------------------------------------------------------
+# LM-head top-k epilogue (q4_gemv_topk)
+# --------------------------------------------------------------------------
+
+def select_topk(y_row, topk):
+    """The topk entries of one row of logits in the order the epilogue defines:
+    value descending (+0 above -0, NaN last), then row ascending."""
+    v = y_row.astype(np.float32)
+    order = np.lexsort((np.arange(len(v)), np.signbit(v), -v.astype(np.float64)))
+    return order[:topk]
+
+
+TOPK_CASES = [(1, 1, 256, 1), (1, 5, 1024, 5), (1, 33, 96, 20), (1, 1000, 1024, 20),
+              (1, 4099, 2560, 32), (1, 70001, 1024, 20), (1, 3000, 8192, 7),
+              (2, 1000, 256, 20), (5, 4099, 1024, 1), (8, 70001, 2560, 20), (8, 64, 96, 32)]
+
+
+@pytest.mark.parametrize("m,n,k,topk", TOPK_CASES, ids=["m%d-n%d-k%d-top%d" % c for c in TOPK_CASES])
+def test_gemv_topk_selects_from_the_gemv_logits(q4, orc, m, n, k, topk):
+    """The selection is exact on the kernel's own fp32 logits (those of q4_gemv, bit for
+    bit); the selected logits are also within tolerance of the oracle's."""
+    x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m * 3 + n + k + topk)
+    xg, pg, sg = gpu(x), gpu(packed), gpu(scales.view(np.float16))
+    _log("q4_gemv_topk m=%d n=%d k=%d topk=%d" % (m, n, k, topk))
+    values, rows = q4.q4_gemv_topk(xg, pg, sg, topk)
+    logits = q4.q4_gemv(xg, pg, sg)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    vals, rws = values.cpu().numpy(), rows.cpu().numpy()
+    for i in range(m):
+        want = select_topk(lg[i], topk)
+        assert np.array_equal(rws[i], want), "token %d rows %s != %s" % (i, rws[i][:8], want[:8])
+        assert np.array_equal(vals[i].view(np.uint32), lg[i][want].view(np.uint32))
+        assert_within(vals[i].astype(np.float64), y_ref[i][want], bound[i][want], "topk values")
+
+
+@pytest.mark.parametrize("m,n", [(1, 300), (1, 5000), (3, 5000)])
+def test_gemv_topk_ties(q4, orc, m, n):
+    """Equal logits rank by row.  5000 equal rows exceed the candidate buffer
+    of the final merge, so that case also takes its merge-everything route."""
+    rng = np.random.default_rng(90 + n + m)
+    k = 256
+    base = (rng.standard_normal((1, k)) * 0.05).astype(np.float32)
+    w = np.repeat(base, n, axis=0)                         # identical rows
+    packed, scales = orc.quantize(w)
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    _log("q4_gemv_topk ties m=%d n=%d" % (m, n))
+    values, rows = q4.q4_gemv_topk(gpu(x), gpu(packed), gpu(scales.view(np.float16)), 32)
+    for i in range(m):
+        assert np.array_equal(rows.cpu().numpy()[i], np.arange(32))
+        assert len(set(values.cpu().numpy()[i].tolist())) == 1
+
+
+def test_gemv_topk_zero_weights(q4, orc):
+    rng = np.random.default_rng(93)
+    k = 256
+    x = rng.standard_normal((1, k)).astype(np.float16)
+    # all-zero weights: every logit is the same zero, so the rows tie
+    zp, zs = orc.quantize(np.zeros((100, k), np.float32))
+    values, rows = q4.q4_gemv_topk(gpu(x), gpu(zp), gpu(zs.view(np.float16)), 10)
+    assert np.array_equal(rows.cpu().numpy()[0], np.arange(10))
+
+
+def test_gemv_topk_deterministic_and_errors(q4, orc):
+    x, packed, scales, _, _ = _case(orc, 1, 5000, 1024, seed=91)
+    xg, pg, sg = gpu(x), gpu(packed), gpu(scales.view(np.float16))
+    a = q4.q4_gemv_topk(xg, pg, sg, 20)
+    b = q4.q4_gemv_topk(xg, pg, sg, 20)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv_topk(xg, pg, sg, 33)
+    small = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(q4.Q4Error) as err:
+        q4.q4_gemv_topk(xg, pg, sg, 5, workspace=small)
+    assert err.value.status == q4.Q4_ERR_WORKSPACE
+    assert q4.q4_gemv_topk_workspace_size(1, 5000, 1024) > 0
+
+
+@pytest.mark.parametrize("key,m,topk", [("decode_08b", 1, 20), ("decode_4b", 8, 20)])
+def test_gemv_topk_lm_head_full_size(q4, key, m, topk):
+    """The full LM head: the fused selection equals the selection on q4_gemv's logits."""
+    mat = qi.WORKLOADS[key].cases[-1][0]
+    _log("topk %s m=%d: generating" % (mat.name, m))
+    w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)
+    packed, scales = q4.q4_quantize(gpu(w))
+    del w
+    xg = gpu(qi.activations(m, mat.k))
+    values, rows = q4.q4_gemv_topk(xg, packed, scales, topk)
+    lg = q4.q4_gemv(xg, packed, scales).cpu().numpy()
+    torch.cuda.synchronize()
+    for i in range(m):
+        want = select_topk(lg[i], topk)
+        assert np.array_equal(rows.cpu().numpy()[i], want)
+        assert np.array_equal(values.cpu().numpy()[i].view(np.uint32), lg[i][want].view(np.uint32))
+
+
+# --------------------------------------------------------------------------
 # fp16 weights (q4_gemv_f16)
 # --------------------------------------------------------------------------
 
