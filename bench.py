@@ -25,7 +25,8 @@ detail   = the other halves of the hot path measured in the same run: the 4B
            LM head (k = 2560), the 0.8B LM head with its top-20 epilogue
            (q4_gemv_topk, against q4_gemv + torch.topk), the 0.8B LM head in
            the fp16 weight format (q4_gemv_f16, 2 bytes per weight), the
-           M = 512 prefill GEMM (TFLOP/s against the
+           M = 512 prefill GEMM, the six 4B projections of one M = 512 batch
+           in one q4_gemm_multi launch (against six q4_gemm launches) (TFLOP/s against the
            2.5 PFLOP/s dense fp16 MFMA peak) and the quantizer (GB/s); --all
            adds the 4B decode set, the M = 8 verify LM head and the
            M = 16/128/2048 prefill GEMMs
@@ -451,6 +452,45 @@ def topk_rate(torch, q4, lib, mat, m, topk, iters):
     return out
 
 
+def gemm_multi_rate(torch, q4, lib, mats, m, iters):
+    """The projections of one prefill batch: one q4_gemm_multi launch against one
+    q4_gemm launch per matrix (weights resident; activations with outliers)."""
+    import q4_inputs as qi
+    x = torch.from_numpy(qi.activations(m, mats[0].k, outliers=True)).cuda()
+    prods = [Product(torch, q4, mat, m, x, 1) for mat in mats]
+    multi = MultiArgs(prods, 0)
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def grouped():
+        st = lib.q4_gemm_multi(x.data_ptr(), m, multi.k, multi.count, multi.packed,
+                               multi.scales, multi.y, multi.n, sh)
+        if st != 0:
+            raise RuntimeError("q4_gemm_multi failed with status %d" % st)
+
+    def separate():
+        for p in prods:
+            launch(lib, "q4_gemm", p.args(0), sh)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters / 1e3
+    tg, ts = timed(grouped), timed(separate)
+    flops = sum(p.flops for p in prods)
+    del prods
+    torch.cuda.empty_cache()
+    return {"matrices": [mat.name for mat in mats], "m": m, "us_grouped": round(tg * 1e6, 3),
+            "us_separate": round(ts * 1e6, 3), "TFLOP_s_grouped": round(flops / tg / 1e12, 2),
+            "mfma_frac_grouped": round(flops / tg / 1e12 / FP16_MFMA_PEAK_TFS, 4)}
+
+
 def gemm_case(torch, q4, lib, mat, m, outliers, iters):
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
@@ -601,6 +641,9 @@ def main() -> int:
     detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
     log("prefill GEMM M=512")
     detail["gemm_m512"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
+    log("grouped prefill GEMM: 4B projections, M=512")
+    detail["gemm_multi_4b_proj_m512"] = gemm_multi_rate(torch, q4, lib, list(qi.DECODE_4B[:-1]),
+                                                        512, 50)
     log("quantize 0.8B LM head")
     detail["quantize_lm_head_08b"] = quantize_rate(torch, q4, qi.DECODE_08B[-1], 10)
     if args.all:

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 4
+#define Q4_ABI_VERSION 5
 #define Q4_GROUP 32
 #define Q4_MULTI_MAX 8
 #define Q4_TOPK_MAX 32
@@ -187,6 +187,18 @@ q4_status q4_gemv_topk(const uint16_t* x, const uint8_t* packed,
 q4_status q4_gemm(const uint16_t* x, const uint8_t* packed,
                   const uint16_t* scales, float* y,
                   int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * q4_gemm_multi -- q4_gemm for several matrices over the same token batch in
+ * one launch: all projections that read one input during prefill (QORA-4B
+ * article, GPU prefill section: the projections of a token batch computed
+ * together on the GPU).  Arguments as q4_gemv_multi, with any m >= 1 (m <= 8
+ * takes the q4_gemv_multi path).  Each y[i] is bit-identical to what q4_gemm
+ * returns for matrix i alone.
+ */
+q4_status q4_gemm_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
+                        const uint8_t* const* packed, const uint16_t* const* scales,
+                        float* const* y, const int64_t* n, void* stream);
 
 #ifdef __cplusplus
 }

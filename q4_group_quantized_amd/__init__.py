@@ -10,6 +10,7 @@ Functions keep the C names:
   q4_gemv(x, packed, scales)           -> y fp32 [m,n]     (1 <= m <= 8)
   q4_gemm(x, packed, scales)           -> y fp32 [m,n]     (any m >= 1)
   q4_gemv_multi(x, [(packed, scales), ...]) -> [y_i fp32 [m,n_i]]  (shared x, <= 8 matrices)
+  q4_gemm_multi(x, [(packed, scales), ...]) -> [y_i fp32 [m,n_i]]  (shared x, any m)
   q4_gemv_f16(x, w)                    -> y fp32 [m,n]     (fp16 weights, 1 <= m <= 8)
   q4_gemv_topk(x, packed, scales, topk) -> (values fp32 [m,topk], rows int32 [m,topk])
   q4_gemv_topk_workspace_size(m, n, k) -> bytes of device workspace q4_gemv_topk needs
@@ -26,7 +27,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4.so")
 
 EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm",
-            "q4_gemv_multi", "q4_gemv_f16", "q4_gemv_topk", "q4_gemv_topk_workspace_size")
+            "q4_gemv_multi", "q4_gemm_multi", "q4_gemv_f16", "q4_gemv_topk",
+            "q4_gemv_topk_workspace_size")
 (Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE,
  Q4_ERR_WORKSPACE) = range(7)
 TOPK_MAX = 32
@@ -63,8 +65,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [p, p, p, p, i64, i64, i64, p]
         fn.restype = ctypes.c_int
-    lib.q4_gemv_multi.argtypes = [p, i64, i64, ctypes.c_int32, p, p, p, p, p]
-    lib.q4_gemv_multi.restype = ctypes.c_int
+    for name in ("q4_gemv_multi", "q4_gemm_multi"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, i64, i64, ctypes.c_int32, p, p, p, p, p]
+        fn.restype = ctypes.c_int
     lib.q4_gemv_f16.argtypes = [p, p, p, i64, i64, i64, p]
     lib.q4_gemv_f16.restype = ctypes.c_int
     lib.q4_gemv_topk_workspace_size.argtypes = [i64, i64, i64]
@@ -164,6 +168,15 @@ def q4_gemv_multi(x, mats, out=None, stream=None):
 
     mats: sequence of (packed, scales) pairs with the same k; returns the list
     of y_i [m, n_i] (or fills ``out``, a list of fp32 [m, n_i] tensors)."""
+    return _multi("q4_gemv_multi", x, mats, out, stream)
+
+
+def q4_gemm_multi(x, mats, out=None, stream=None):
+    """Prefill products of several matrices over the same token batch in one launch."""
+    return _multi("q4_gemm_multi", x, mats, out, stream)
+
+
+def _multi(name, x, mats, out, stream):
     import torch
     _require(x, torch.float16, "x")
     if x.dim() != 2:
@@ -192,9 +205,9 @@ def q4_gemv_multi(x, mats, out=None, stream=None):
     y_a = ptrs(*[y.data_ptr() for y in ys])
     n_a = (ctypes.c_int64 * max(count, 1))(*[p.shape[0] for p, _ in mats])
     with torch.cuda.device(x.device):
-        st = load().q4_gemv_multi(x.data_ptr(), m, k, count, packed_a, scales_a, y_a, n_a,
-                                  _stream(stream, x.device))
-    _check("q4_gemv_multi", st)
+        st = getattr(load(), name)(x.data_ptr(), m, k, count, packed_a, scales_a, y_a, n_a,
+                                   _stream(stream, x.device))
+    _check(name, st)
     return ys
 
 

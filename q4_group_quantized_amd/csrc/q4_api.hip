@@ -119,18 +119,33 @@ q4_status q4_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* scal
                                       static_cast<hipStream_t>(stream)));
 }
 
-q4_status q4_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
-                        const uint8_t* const* packed, const uint16_t* const* scales,
-                        float* const* y, const int64_t* n, void* stream) {
+q4_status check_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
+                      const uint8_t* const* packed, const uint16_t* const* scales,
+                      float* const* y, const int64_t* n, int64_t m_max) {
     if (!packed || !scales || !y || !n) return Q4_ERR_NULL;
     if (count < 1 || count > Q4_MULTI_MAX) return Q4_ERR_SHAPE;
     for (int32_t i = 0; i < count; ++i) {
-        const q4_status st = check_product(x, packed[i], scales[i], y[i], m, n[i], k, 8);
+        const q4_status st = check_product(x, packed[i], scales[i], y[i], m, n[i], k, m_max);
         if (st != Q4_OK) return st;
     }
-    q4_status st = device_ok();
+    return device_ok();
+}
+
+q4_status q4_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
+                        const uint8_t* const* packed, const uint16_t* const* scales,
+                        float* const* y, const int64_t* n, void* stream) {
+    const q4_status st = check_multi(x, m, k, count, packed, scales, y, n, 8);
     if (st != Q4_OK) return st;
     return map_launch(q4::launch_gemv_multi(x, m, k, count, packed, scales, y, n,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+q4_status q4_gemm_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
+                        const uint8_t* const* packed, const uint16_t* const* scales,
+                        float* const* y, const int64_t* n, void* stream) {
+    const q4_status st = check_multi(x, m, k, count, packed, scales, y, n, kMaxN);
+    if (st != Q4_OK) return st;
+    return map_launch(q4::launch_gemm_multi(x, m, k, count, packed, scales, y, n,
                                             static_cast<hipStream_t>(stream)));
 }
 

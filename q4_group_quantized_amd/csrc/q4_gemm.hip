@@ -30,6 +30,7 @@
 // Rows past M, columns past N and groups past G are clamped to real
 // addresses: their results are never stored, and out-of-range groups are
 // never computed.
+#include "q4.h"
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
 
@@ -66,24 +67,53 @@ struct Gemm {
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
 };
 
+// The matrices of one launch: up to kGemmMaxSegments weight matrices over the
+// same activations (one for q4_gemm).  Segment s owns workgroups
+// [tile0[s], tile0[s] + tiles[s]); a tile's work and its order of fp32 sums
+// depend only on its index inside its segment, so every matrix gets the
+// result a launch of its own would give, bit for bit.
+constexpr int kGemmMaxSegments = 8;
+struct GemmSegments {
+    const uint8_t* packed[kGemmMaxSegments];
+    const uint16_t* scales[kGemmMaxSegments];
+    float* y[kGemmMaxSegments];
+    int64_t n[kGemmMaxSegments];
+    int64_t tiles_n[kGemmMaxSegments];
+    int64_t tile0[kGemmMaxSegments];
+    int count;
+};
+static_assert(kGemmMaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MULTI_MAX matrices");
+
 // At least two waves per SIMD: caps a wave at 256 registers, which also makes
 // the compiler keep MFMA results in VGPRs instead of routing them through
 // AGPRs (four v_accvgpr_read per 16x16 block before the scale FMAs).
 template <int BM, int WN, int WK, int KG, int S>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, float* __restrict__ y, int M, int64_t N, int K,
-    int G, int64_t tiles_n, SpliceConsts kc) {
+    const uint16_t* __restrict__ x, GemmSegments seg, int M, int K, int G, SpliceConsts kc) {
     using C = Gemm<BM, WN, WK, KG, S>;
     constexpr int MB = C::MB;
     extern __shared__ __align__(16) unsigned char smem[];
+
+    // this workgroup's matrix (selects over constant indices, workgroup-uniform)
+    const uint8_t* packed = seg.packed[0];
+    const uint16_t* scales = seg.scales[0];
+    float* y = seg.y[0];
+    int64_t N = seg.n[0], tiles_n = seg.tiles_n[0], tile0 = seg.tile0[0];
+#pragma unroll
+    for (int i = 1; i < kGemmMaxSegments; ++i) {
+        if (i < seg.count && (int64_t)blockIdx.x >= seg.tile0[i]) {
+            packed = seg.packed[i]; scales = seg.scales[i]; y = seg.y[i];
+            N = seg.n[i]; tiles_n = seg.tiles_n[i]; tile0 = seg.tile0[i];
+        }
+    }
+    const int64_t tile = (int64_t)blockIdx.x - tile0;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wn = wave % WN;
     const int kp = wave / WN;
-    const int64_t nt0 = ((int64_t)blockIdx.x % tiles_n) * C::BN;     // tile's first column
-    const int64_t m0 = ((int64_t)blockIdx.x / tiles_n) * BM;
+    const int64_t nt0 = (tile % tiles_n) * C::BN;     // tile's first column
+    const int64_t m0 = (tile / tiles_n) * BM;
 
     const int Gp = (G + WK - 1) / WK;                     // groups per K slice
     const int gbeg = kp * Gp;
@@ -94,7 +124,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     // Workgroups start their walk over K at different stages so that the CUs
     // sharing an L2 do not all request the same activation columns at once.
     // The order of the fp32 sums changes with it, identically on every run.
-    const int rot = (int)(blockIdx.x % (uint32_t)nstages);
+    const int rot = (int)(tile % nstages);
     auto stage_group = [&](int st) {               // first group (in the slice) of stage st
         const int r = st + rot;
         return (r < nstages ? r : r - nstages) * KG;
@@ -256,11 +286,22 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
 }
 
 template <int BM, int WN, int WK, int KG, int S>
-hipError_t launch_gemm_t(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
-                         float* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* packed,
+                         const uint16_t* const* scales, float* const* y, const int64_t* n,
+                         int64_t m, int64_t k, hipStream_t stream) {
     using C = Gemm<BM, WN, WK, KG, S>;
-    const int64_t tiles_n = (n + C::BN - 1) / C::BN;
-    const int64_t tiles = tiles_n * ((m + BM - 1) / BM);
+    GemmSegments seg = {};
+    seg.count = count;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        seg.packed[i] = packed[i];
+        seg.scales[i] = scales[i];
+        seg.y[i] = y[i];
+        seg.n[i] = n[i];
+        seg.tiles_n[i] = (n[i] + C::BN - 1) / C::BN;
+        seg.tile0[i] = tiles;
+        tiles += seg.tiles_n[i] * ((m + BM - 1) / BM);
+    }
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     static bool attr_set = false;
     if (!attr_set) {
@@ -271,9 +312,21 @@ hipError_t launch_gemm_t(const uint16_t* x, const uint8_t* packed, const uint16_
         attr_set = true;
     }
     hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
-                       dim3(C::kThreads), C::kLdsBytes, stream, x, packed, scales, y, (int)m, n,
-                       (int)k, (int)(k / 32), tiles_n, kSpliceConsts);
+                       dim3(C::kThreads), C::kLdsBytes, stream, x, seg, (int)m, (int)k,
+                       (int)(k / 32), kSpliceConsts);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* const* packed,
+                                const uint16_t* const* scales, float* const* y,
+                                const int64_t* n, int64_t m, int64_t k, hipStream_t stream) {
+    if (m <= 16)
+        return launch_gemm_t<16, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
+    if (m <= 32)
+        return launch_gemm_t<32, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
+    if (m < 256)
+        return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+    return launch_gemm_t<128, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
 }
 
 }  // namespace
@@ -281,10 +334,14 @@ hipError_t launch_gemm_t(const uint16_t* x, const uint8_t* packed, const uint16_
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
                        float* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
     if (m <= 8) return launch_gemv(x, packed, scales, y, m, n, k, stream);
-    if (m <= 16) return launch_gemm_t<16, 1, 4, 2, 4>(x, packed, scales, y, m, n, k, stream);
-    if (m <= 32) return launch_gemm_t<32, 1, 4, 2, 4>(x, packed, scales, y, m, n, k, stream);
-    if (m < 256) return launch_gemm_t<64, 2, 4, 2, 2>(x, packed, scales, y, m, n, k, stream);
-    return launch_gemm_t<128, 2, 4, 2, 2>(x, packed, scales, y, m, n, k, stream);
+    return launch_gemm_segments(x, 1, &packed, &scales, &y, &n, m, k, stream);
+}
+
+hipError_t launch_gemm_multi(const uint16_t* x, int64_t m, int64_t k, int count,
+                             const uint8_t* const* packed, const uint16_t* const* scales,
+                             float* const* y, const int64_t* n, hipStream_t stream) {
+    if (m <= 8) return launch_gemv_multi(x, m, k, count, packed, scales, y, n, stream);
+    return launch_gemm_segments(x, count, packed, scales, y, n, m, k, stream);
 }
 
 }  // namespace q4

@@ -46,6 +46,11 @@ hipError_t launch_gemv_topk(const uint16_t* x, const uint8_t* packed, const uint
                             int64_t m, int64_t n, int64_t k, int topk, float* values,
                             int32_t* rows, void* workspace, hipStream_t stream);
 
+// count (1..8) matrices sharing x and k, any m >= 1; host arrays.
+hipError_t launch_gemm_multi(const uint16_t* x, int64_t m, int64_t k, int count,
+                             const uint8_t* const* packed, const uint16_t* const* scales,
+                             float* const* y, const int64_t* n, hipStream_t stream);
+
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed,
                        const uint16_t* scales, float* y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream);

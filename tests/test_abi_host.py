@@ -145,12 +145,13 @@ def test_gemv_topk_workspace_size_without_device(lib):
     assert lib.q4_gemv_topk_workspace_size(1, 64, 48) == 0      # invalid shape
 
 
-def _multi(lib, x, m, k, packed, scales, y, n, count=None):
-    """Call q4_gemv_multi with host arrays built from Python lists (None = NULL array)."""
+def _multi(lib, x, m, k, packed, scales, y, n, count=None, fn="q4_gemv_multi"):
+    """Call q4_gemv_multi (or q4_gemm_multi) with host arrays built from Python lists
+    (None = NULL array)."""
     def arr(vals, ctype):
         return None if vals is None else (ctype * max(len(vals), 1))(*vals)
     cnt = len(n) if count is None else count
-    return lib.q4_gemv_multi(x, m, k, cnt, arr(packed, ctypes.c_void_p),
+    return getattr(lib, fn)(x, m, k, cnt, arr(packed, ctypes.c_void_p),
                              arr(scales, ctypes.c_void_p), arr(y, ctypes.c_void_p),
                              arr(n, ctypes.c_int64), None)
 
@@ -184,9 +185,28 @@ def test_gemv_multi_rejects_bad_arguments(lib, case, expect):
     assert _multi(lib, **args) == expect
 
 
+@pytest.mark.parametrize("case,expect", [
+    (dict(packed=None), 1),
+    (dict(y=[FAKE, NULL]), 1),
+    (dict(count=0), 2),
+    (dict(count=9, packed=[FAKE] * 9, scales=[FAKE] * 9, y=[FAKE] * 9, n=[8] * 9), 2),
+    (dict(m=0), 2),
+    (dict(k=48), 2),
+    (dict(n=[8, 0]), 2),
+    (dict(x=FAKE + 2), 3),
+    (dict(scales=[FAKE + 1, FAKE]), 3),
+])
+def test_gemm_multi_rejects_bad_arguments(lib, case, expect):
+    args = dict(x=FAKE, m=40, k=64, packed=[FAKE, FAKE], scales=[FAKE, FAKE], y=[FAKE, FAKE],
+                n=[8, 8], count=None)
+    args.update(case)
+    assert _multi(lib, **args, fn="q4_gemm_multi") == expect
+
+
 def test_binding_names_match_the_c_abi():
     import q4_group_quantized_amd as q4
-    for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_gemv_multi", "q4_gemv_f16",
+    for name in ("q4_quantize", "q4_gemv", "q4_gemm", "q4_gemv_multi", "q4_gemm_multi",
+                 "q4_gemv_f16",
                  "q4_gemv_topk", "q4_gemv_topk_workspace_size", "q4_status_str",
                  "q4_abi_version"):
         assert callable(getattr(q4, name))

@@ -260,6 +260,63 @@ def test_gemv_multi_binding_errors(q4):
         q4.q4_gemv_multi(x, [(p, s), (p[:, :16], s[:, :1])])
 
 
+GEMM_MULTI_SETS = [
+    (9, 256, (15, 100)),
+    (40, 1056, (33, 7, 64)),
+    (128, 2560, (130, 5, 257, 64)),
+    (300, 96, (17, 200, 3, 1, 70, 33, 9, 129)),            # eight matrices
+    (512, 1024, (100, 61)),
+    (3, 256, (15, 100)),                                   # m <= 8: the q4_gemv_multi path
+]
+
+
+@pytest.mark.parametrize("m,k,ns", GEMM_MULTI_SETS, ids=["m%d-k%d-%dmat" % (c[0], c[1], len(c[2]))
+                                                         for c in GEMM_MULTI_SETS])
+def test_gemm_multi(q4, orc, m, k, ns):
+    """Each output against the oracle, and bit-identical to q4_gemm alone."""
+    rng = np.random.default_rng(m * 11 + k + len(ns))
+    x = (rng.standard_normal((m, k)) * 2).astype(np.float16)
+    mats, refs = [], []
+    for i, n in enumerate(ns):
+        w = oracle_pins.spread_weights(rng, n, k) if i % 2 else \
+            (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        packed, scales = orc.quantize(w)
+        mats.append((gpu(packed), gpu(scales.view(np.float16))))
+        refs.append(orc.matmul(x, packed, scales))
+    _log("q4_gemm_multi m=%d k=%d n=%s" % (m, k, ns))
+    xg = gpu(x)
+    ys = q4.q4_gemm_multi(xg, mats)
+    torch.cuda.synchronize()
+    for i, (y, (y_ref, bound)) in enumerate(zip(ys, refs)):
+        assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound,
+                      "gemm multi matrix %d (n=%d)" % (i, ns[i]))
+        alone = q4.q4_gemm(xg, *mats[i])
+        torch.cuda.synchronize()
+        assert torch.equal(y, alone), "gemm multi matrix %d differs from q4_gemm" % i
+
+
+def test_gemm_multi_layer_projections_full_size(q4, orc):
+    """The six 4B projections of the decode set over one prefill batch (m = 512,
+    outlier activations) in one launch: sampled rows against the oracle, every
+    output bit-identical to q4_gemm alone."""
+    wl = qi.WORKLOADS["decode_4b"]
+    x = qi.activations(512, wl.cases[0][0].k, outliers=True)
+    xg = gpu(x)
+    mats, samples = [], []
+    for mat, _ in wl.cases[:-1]:
+        w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)
+        mats.append(q4.q4_quantize(gpu(w)))
+        rows = _sample_rows(mat.n, np.random.default_rng(mat.tensor_id), count=96)
+        samples.append((rows, orc.quantize(w[rows])))
+    _log("q4_gemm_multi: %d projections, m=512" % len(mats))
+    ys = q4.q4_gemm_multi(xg, mats)
+    torch.cuda.synchronize()
+    for (mat, _), y, (p, s_), (rows, (rp, rs)) in zip(wl.cases, ys, mats, samples):
+        assert torch.equal(y, q4.q4_gemm(xg, p, s_)), mat.name
+        y_ref, bound = orc.matmul(x, rp, rs)
+        assert_within(y.cpu().numpy().astype(np.float64)[:, rows], y_ref, bound, mat.name)
+
+
 @pytest.mark.parametrize("key", ["decode_08b", "decode_4b"])
 def test_gemv_multi_decode_set_full_size(q4, orc, key):
     """A whole decode set (seven matrices incl. the LM head) in one call, at
