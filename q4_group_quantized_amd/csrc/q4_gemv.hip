@@ -34,8 +34,8 @@
 // m = 1 has its own streaming kernel (gemv1_kernel below): there the block-
 // diagonal MFMA would waste 15/16 of the matrix core anyway, and what bounds
 // the kernel is how sequentially each wave walks HBM.  Every wave owns a
-// contiguous range of rows and reads it front to back, one wave per SIMD;
-// LPR = 16, 8 or 32 lanes share a row, each lane owning the same
+// contiguous range of rows and reads it front to back, one or two waves per
+// SIMD (see gemv1_waves_per_simd); LPR = 16, 8 or 32 lanes share a row, each lane owning the same
 // GPL = K / (32 LPR) groups of every row, so its activations stay in
 // registers for the whole kernel.  Per group: 16-byte code load, the 16-entry
 // table lookup as fp16 pairs (unpack8_split), v_dot2_f32_f16 against the
@@ -56,6 +56,10 @@ constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kTileGroups = 8;                  // groups per tile (two sets of 4)
 constexpr int kLdsBudget = 64 * 1024;           // bytes of LDS for activations
 constexpr int kPrefetch = 4;                    // tiles in flight per wave
+// Halves of padding after each token's activations in LDS: with rows of
+// 64-byte groups the token stride would be a multiple of the 256-byte bank
+// span, so the four tokens read by one MFMA operand would hit the same banks.
+constexpr int kTokenPad = 8;
 
 struct Tile {
     u32x4_t p0;      // group j0 + kb
@@ -87,8 +91,9 @@ __device__ __forceinline__ Tile load_tile(const uint8_t* __restrict__ prow,
     return t;
 }
 
-// xs: LDS activations [TB*4 tokens][cg groups][32 halves, unpack order],
-// followed by 32 zero halves that off-diagonal lanes read as their A operand.
+// xs: LDS activations [TB*4 tokens][cg groups][32 halves, unpack order], each
+// token's row followed by kTokenPad halves, then 32 zero halves that
+// off-diagonal lanes read as their A operand.
 template <int TB>
 __device__ __forceinline__ void compute_tile(const Tile& t, const _Float16* xs,
                                              int cg, int jl0, int lane,
@@ -112,8 +117,8 @@ __device__ __forceinline__ void compute_tile(const Tile& t, const _Float16* xs,
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             const half8_t* src = reinterpret_cast<const half8_t*>(
-                diag ? xs + ((size_t)(4 * tb + tau_a) * cg + jl) * 32
-                     : xs + (size_t)TB * 4 * cg * 32);
+                diag ? xs + (size_t)(4 * tb + tau_a) * (cg * 32 + kTokenPad) + jl * 32
+                     : xs + (size_t)TB * 4 * (cg * 32 + kTokenPad));
 #pragma unroll
             for (int q = 0; q < 4; ++q) a[tb][q] = src[q];
             float4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -142,10 +147,11 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, _Float16
         const int j = jc0 + jl;
         if (tok < M && j < G)
             v = *reinterpret_cast<const u32x4_t*>(x + (size_t)tok * K + 32 * j + 8 * q);
-        *reinterpret_cast<u32x4_t*>(xs + ((size_t)tok * cg + jl) * 32 + 8 * q) = permute_x8(v);
+        *reinterpret_cast<u32x4_t*>(xs + (size_t)tok * (cg * 32 + kTokenPad) + jl * 32 + 8 * q) =
+            permute_x8(v);
     }
     if (threadIdx.x < 4)
-        *reinterpret_cast<u32x4_t*>(xs + (size_t)TB * 4 * cg * 32 + 8 * threadIdx.x) =
+        *reinterpret_cast<u32x4_t*>(xs + (size_t)TB * 4 * (cg * 32 + kTokenPad) + 8 * threadIdx.x) =
             u32x4_t{0u, 0u, 0u, 0u};
 }
 
@@ -306,7 +312,8 @@ hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
     const int G = k / 32;
     const int gpad = (G + 7) & ~7;
     const int per_group_bytes = TB * 4 * 64;
-    int chunk = (kLdsBudget / per_group_bytes) & ~7;
+    const int fixed_bytes = TB * 4 * kTokenPad * 2 + 64;     // token pads, zero block
+    int chunk = ((kLdsBudget - fixed_bytes) / per_group_bytes) & ~7;
     if (chunk > gpad) chunk = gpad;
     const int nchunks = (gpad + chunk - 1) / chunk;
     const int64_t RB = (n + 15) / 16;
@@ -323,7 +330,7 @@ hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
     }
     const int64_t blocks64 = (waves + kGemvWaves - 1) / kGemvWaves;
     const int blocks = (int)(blocks64 > 0 ? blocks64 : 1);
-    const size_t lds = (size_t)per_group_bytes * chunk + 64;
+    const size_t lds = (size_t)per_group_bytes * chunk + fixed_bytes;
     hipLaunchKernelGGL((gemv_kernel<TB, kScale16>), dim3(blocks), dim3(kGemvThreads), lds,
                        stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB);
     return hipGetLastError();
@@ -528,18 +535,27 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
     }
 }
 
-// Steps in flight per wave: about 16 code loads per lane outstanding.
+// Steps in flight per wave and waves per SIMD of the plain launch, from a
+// sweep on the LM heads (all variants bit-identical): at K = 1024 (2 groups
+// per lane) four steps x two waves per SIMD, at K = 2560 (5 groups per lane)
+// two steps x one wave per SIMD were fastest -- about 10-16 KB of code loads
+// in flight per SIMD, split so that one wave's unpacking overlaps the other's
+// loads where a step is short.
 constexpr int gemv1_prefetch(int gpl) {
+    return gpl <= 1 ? 8 : gpl == 2 ? 4 : gpl == 3 ? 3 : 2;
+}
+constexpr int gemv1_waves_per_simd(int gpl) { return gpl <= 3 ? 2 : 1; }
+// The top-k variant (more work per step, LDS buffers) keeps one wave per SIMD
+// with about 16 code loads per lane in flight.
+constexpr int gemv1_topk_prefetch(int gpl) {
     return gpl <= 2 ? 8 : gpl == 3 ? 6 : gpl <= 5 ? 4 : gpl <= 7 ? 3 : 2;
 }
 
-// One wave per SIMD: fewer, longer sequential streams measured faster than
-// more waves each with a shorter range.
 template <int LPR, int GPL>
 hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* const* packed,
                           const uint16_t* const* scales, float* const* y, const int64_t* n,
                           uint64_t* partials, hipStream_t stream) {
-    constexpr int PF = gemv1_prefetch(GPL);
+    constexpr int PF = gemv1_prefetch(GPL), PFT = gemv1_topk_prefetch(GPL);
     constexpr int RPS = 64 / LPR;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -548,7 +564,8 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
     seg.count = count;
     int64_t total_rq = 0;
     for (int s = 0; s < count; ++s) total_rq += (n[s] + RPS - 1) / RPS;
-    const int64_t max_waves = (int64_t)device_info(dev).cu_count * kGemvWaves;
+    const int wps = partials ? 1 : gemv1_waves_per_simd(GPL);
+    const int64_t max_waves = (int64_t)device_info(dev).cu_count * kGemvWaves * wps;
     const int64_t per = (total_rq + max_waves - 1) / max_waves;   // steps per wave
     int64_t wave0 = 0;
     for (int s = 0; s < count; ++s) {
@@ -566,7 +583,7 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
     }
     const int blocks = (int)((wave0 + kGemvWaves - 1) / kGemvWaves);
     if (partials)
-        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, true>), dim3(blocks), dim3(kGemvThreads),
+        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PFT, true>), dim3(blocks), dim3(kGemvThreads),
                            0, stream, x, k, seg, kSpliceConsts, partials);
     else
         hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, false>), dim3(blocks), dim3(kGemvThreads),
@@ -632,8 +649,8 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed,
 
 int64_t gemv1_topk_lists(int64_t n, int64_t k, int cu_count) {
     if (gemv1_lanes_per_row(k) == 0) return 0;
-    // the m = 1 launcher's grid for one matrix of n rows: at most one wave per
-    // SIMD, rounded up to whole workgroups
+    // the m = 1 launcher's grid for one matrix of n rows in its top-k form: at
+    // most one wave per SIMD, rounded up to whole workgroups
     const int lpr = gemv1_lanes_per_row(k);
     const int64_t rq = (n + 64 / lpr - 1) / (64 / lpr);
     const int64_t max_waves = (int64_t)cu_count * kGemvWaves;
