@@ -374,21 +374,21 @@ def lm_head_rate(torch, q4, lib, mat, iters):
     return out
 
 
-def f16_gemv_rate(torch, q4, lib, mat, m, iters):
-    """Back-to-back q4_gemv_f16 launches over rotated fp16 weight copies."""
+def f16_gemv_rate(torch, q4, lib, mat, m, iters, fn="q4_gemv_f16", outliers=False):
+    """Back-to-back q4_gemv_f16 (or q4_gemm_f16) launches over rotated fp16 weight copies."""
     import q4_inputs as qi
-    x = torch.from_numpy(qi.activations(m, mat.k)).cuda()
+    x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
     w0 = torch.from_numpy(qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)).cuda().half()
     copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 2)))
     ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     y = torch.empty((m, mat.n), dtype=torch.float32, device=x.device)
     sh = torch.cuda.current_stream().cuda_stream
+    call = getattr(lib, fn)
 
     def go(i):
-        st = lib.q4_gemv_f16(x.data_ptr(), ws[i % copies].data_ptr(), y.data_ptr(), m, mat.n,
-                             mat.k, sh)
+        st = call(x.data_ptr(), ws[i % copies].data_ptr(), y.data_ptr(), m, mat.n, mat.k, sh)
         if st != 0:
-            raise RuntimeError("q4_gemv_f16 failed with status %d" % st)
+            raise RuntimeError("%s failed with status %d" % (fn, st))
     for i in range(3):
         go(i)
     torch.cuda.synchronize()
@@ -402,9 +402,14 @@ def f16_gemv_rate(torch, q4, lib, mat, m, iters):
     nbytes = mat.n * mat.k * 2 + 2 * m * mat.k + 4 * m * mat.n
     del ws, w0
     torch.cuda.empty_cache()
-    return {"matrix": mat.name + ".f16", "m": m, "n": mat.n, "k": mat.k, "us": round(t * 1e6, 3),
-            "GB_s": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-            "copies": copies}
+    out = {"matrix": mat.name + ".f16", "fn": fn, "m": m, "n": mat.n, "k": mat.k,
+           "us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 1),
+           "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "copies": copies}
+    if m >= 16:
+        tflops = 2.0 * m * mat.n * mat.k / t / 1e12
+        out["TFLOP_s"] = round(tflops, 2)
+        out["mfma_frac"] = round(tflops / FP16_MFMA_PEAK_TFS, 4)
+    return out
 
 
 def topk_rate(torch, q4, lib, mat, m, topk, iters):
@@ -641,6 +646,8 @@ def main() -> int:
     detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
     log("prefill GEMM M=512")
     detail["gemm_m512"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
+    detail["f16_gemm_m512"] = f16_gemv_rate(torch, q4, lib, qi.PREFILL_4B, 512, 100,
+                                            fn="q4_gemm_f16", outliers=True)
     log("grouped prefill GEMM: 4B projections, M=512")
     detail["gemm_multi_4b_proj_m512"] = gemm_multi_rate(torch, q4, lib, list(qi.DECODE_4B[:-1]),
                                                         512, 50)
@@ -663,6 +670,8 @@ def main() -> int:
         detail["lm_head_argmax_4b_m8"] = topk_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 1, 30)
         log("F16 GEMV LM head 4B, M=8")
         detail["f16_gemv_lm_head_4b_m8"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 30)
+        detail["f16_gemm_m2048"] = f16_gemv_rate(torch, q4, lib, qi.PREFILL_4B_WIDE, 2048, 30,
+                                                 fn="q4_gemm_f16")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 5
+#define Q4_ABI_VERSION 6
 #define Q4_GROUP 32
 #define Q4_MULTI_MAX 8
 #define Q4_TOPK_MAX 32
@@ -148,6 +148,21 @@ q4_status q4_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
  * accumulation; the bound |y - y_ref| <= 1e-3 * sum|x * w| + 1e-6 holds.
  */
 q4_status q4_gemv_f16(const uint16_t* x, const uint16_t* w, float* y,
+                      int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * q4_gemm_f16 -- prefill product with fp16 weights: q4_gemv_f16's arguments
+ * and semantics for any m in 1 .. 2^31-1 (m <= 8 runs the decode kernel),
+ * the batched prefill of the QORA-4B article's GPU section over its F16
+ * weight format (quantization section, format table).
+ *   x       [in]  fp16 bits [m, k], device, 16-byte aligned
+ *   w       [in]  fp16 bits [n, k], device, 16-byte aligned
+ *   y       [out] fp32 [m, n], device, 4-byte aligned
+ * k % 32 == 0; m * k and m * n within the element limit of q4_gemm, else
+ * Q4_ERR_SHAPE.  Accuracy as q4_gemv_f16 (exact products, fp32 sums); the
+ * result is deterministic for a given (m, n, k).
+ */
+q4_status q4_gemm_f16(const uint16_t* x, const uint16_t* w, float* y,
                       int64_t m, int64_t n, int64_t k, void* stream);
 
 /*

@@ -12,6 +12,7 @@ Functions keep the C names:
   q4_gemv_multi(x, [(packed, scales), ...]) -> [y_i fp32 [m,n_i]]  (shared x, <= 8 matrices)
   q4_gemm_multi(x, [(packed, scales), ...]) -> [y_i fp32 [m,n_i]]  (shared x, any m)
   q4_gemv_f16(x, w)                    -> y fp32 [m,n]     (fp16 weights, 1 <= m <= 8)
+  q4_gemm_f16(x, w)                    -> y fp32 [m,n]     (fp16 weights, any m)
   q4_gemv_topk(x, packed, scales, topk) -> (values fp32 [m,topk], rows int32 [m,topk])
   q4_gemv_topk_workspace_size(m, n, k) -> bytes of device workspace q4_gemv_topk needs
   q4_status_str(code), q4_abi_version()
@@ -27,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4.so")
 
 EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm",
-            "q4_gemv_multi", "q4_gemm_multi", "q4_gemv_f16", "q4_gemv_topk",
+            "q4_gemv_multi", "q4_gemm_multi", "q4_gemv_f16", "q4_gemm_f16", "q4_gemv_topk",
             "q4_gemv_topk_workspace_size")
 (Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE,
  Q4_ERR_WORKSPACE) = range(7)
@@ -69,8 +70,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [p, i64, i64, ctypes.c_int32, p, p, p, p, p]
         fn.restype = ctypes.c_int
-    lib.q4_gemv_f16.argtypes = [p, p, p, i64, i64, i64, p]
-    lib.q4_gemv_f16.restype = ctypes.c_int
+    for fn in (lib.q4_gemv_f16, lib.q4_gemm_f16):
+        fn.argtypes = [p, p, p, i64, i64, i64, p]
+        fn.restype = ctypes.c_int
     lib.q4_gemv_topk_workspace_size.argtypes = [i64, i64, i64]
     lib.q4_gemv_topk_workspace_size.restype = ctypes.c_size_t
     lib.q4_gemv_topk.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int32, p, p, p,
@@ -213,6 +215,15 @@ def _multi(name, x, mats, out, stream):
 
 def q4_gemv_f16(x, w, out=None, stream=None):
     """Decode product with fp16 weights: y[m, n] = x[m, k] . w[n, k]^T, 1 <= m <= 8."""
+    return _f16("q4_gemv_f16", x, w, out, stream)
+
+
+def q4_gemm_f16(x, w, out=None, stream=None):
+    """Prefill product with fp16 weights: q4_gemv_f16 for any m >= 1."""
+    return _f16("q4_gemm_f16", x, w, out, stream)
+
+
+def _f16(name, x, w, out, stream):
     import torch
     _require(x, torch.float16, "x")
     _require(w, torch.float16, "w")
@@ -227,9 +238,9 @@ def q4_gemv_f16(x, w, out=None, stream=None):
         if tuple(y.shape) != (m, n):
             raise ValueError("out must be [m, n]")
     with torch.cuda.device(x.device):
-        st = load().q4_gemv_f16(x.data_ptr(), w.data_ptr(), y.data_ptr(), m, n, k,
-                                _stream(stream, x.device))
-    _check("q4_gemv_f16", st)
+        st = getattr(load(), name)(x.data_ptr(), w.data_ptr(), y.data_ptr(), m, n, k,
+                                   _stream(stream, x.device))
+    _check(name, st)
     return y
 
 

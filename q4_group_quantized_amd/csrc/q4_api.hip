@@ -160,6 +160,17 @@ q4_status q4_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
     return map_launch(q4::launch_gemv_f16(x, w, y, m, n, k, static_cast<hipStream_t>(stream)));
 }
 
+q4_status q4_gemm_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, int64_t n,
+                      int64_t k, void* stream) {
+    if (!x || !w || !y) return Q4_ERR_NULL;
+    q4_status st = check_nk(n, k);
+    if (st != Q4_OK) return st;
+    if (m < 1 || m > kMaxN || m > kMaxElems / k || m > kMaxElems / n) return Q4_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    if ((st = device_ok()) != Q4_OK) return st;
+    return map_launch(q4::launch_gemm_f16(x, w, y, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
 size_t q4_gemv_topk_workspace_size(int64_t m, int64_t n, int64_t k) {
     if (check_nk(n, k) != Q4_OK || m < 1 || m > 8) return 0;
     int dev = -1;

@@ -34,6 +34,10 @@ hipError_t launch_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int count,
 hipError_t launch_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
                            int64_t n, int64_t k, hipStream_t stream);
 
+// fp16 weights [n, k], any m (m <= 8 -> launch_gemv_f16).
+hipError_t launch_gemm_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
+                           int64_t n, int64_t k, hipStream_t stream);
+
 // Lists of the fused m = 1 top-k GEMV for n rows (0 when k does not fit the
 // streaming kernel), and its launch writing those lists to `partials`.
 int64_t gemv1_topk_lists(int64_t n, int64_t k, int cu_count);

@@ -121,6 +121,25 @@ def test_gemv_f16_rejects_bad_arguments(lib, args, expect):
 
 
 @pytest.mark.parametrize("args,expect", [
+    ((NULL, FAKE, FAKE, 16, 8, 64), 1),
+    ((FAKE, NULL, FAKE, 16, 8, 64), 1),
+    ((FAKE, FAKE, NULL, 16, 8, 64), 1),
+    ((FAKE, FAKE, FAKE, 0, 8, 64), 2),
+    ((FAKE, FAKE, FAKE, -3, 8, 64), 2),
+    ((FAKE, FAKE, FAKE, 1 << 31, 8, 64), 2),
+    ((FAKE, FAKE, FAKE, 16, 0, 64), 2),
+    ((FAKE, FAKE, FAKE, 16, 8, 48), 2),
+    ((FAKE, FAKE, FAKE, 16, 8, 16), 2),
+    ((FAKE + 2, FAKE, FAKE, 16, 8, 64), 3),
+    ((FAKE, FAKE + 8, FAKE, 16, 8, 64), 3),
+    ((FAKE, FAKE, FAKE + 2, 16, 8, 64), 3),
+])
+def test_gemm_f16_rejects_bad_arguments(lib, args, expect):
+    # argument checks run before the device check, so a GPU-less host sees them
+    assert lib.q4_gemm_f16(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
     ((NULL, FAKE, FAKE, 1, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 1),
     ((FAKE, NULL, FAKE, 1, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 1),
     ((FAKE, FAKE, NULL, 1, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20), 1),

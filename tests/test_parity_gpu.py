@@ -515,6 +515,75 @@ def test_gemv_f16_lm_head_full_size(q4, orc, mat, m):
 
 
 # --------------------------------------------------------------------------
+# fp16 weights, any m (q4_gemm_f16)
+# --------------------------------------------------------------------------
+
+F16_GEMM_SHAPES = [(15, 64), (17, 96), (100, 1056), (257, 2560), (61, 4096), (1000, 320)]
+
+
+@pytest.mark.parametrize("n,k", F16_GEMM_SHAPES)
+@pytest.mark.parametrize("m", [9, 16, 17, 32, 33, 64, 100, 255, 256, 300])
+def test_gemm_f16_product(q4, orc, m, n, k):
+    x, w = _f16_case(m, n, k, seed=m * 11 + n + 3 * k)
+    _log("q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
+    y = q4.q4_gemm_f16(gpu(x), gpu(w))
+    torch.cuda.synchronize()
+    y_ref, bound = orc.matmul_f16(x, w)
+    assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound,
+                  "q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
+
+
+def test_gemm_f16_exact_special_inputs(q4):
+    """One-hot activation rows pick weight columns exactly; zero operands give zeros."""
+    rng = np.random.default_rng(79)
+    n, k = 70, 160
+    w = rng.standard_normal((n, k)).astype(np.float16)
+    wg = gpu(w)
+    _log("q4_gemm_f16 one-hot / zero inputs")
+    for m in (16, 40, 160):
+        x = np.eye(k, dtype=np.float16)[:m]
+        y = q4.q4_gemm_f16(gpu(x), wg).cpu().numpy().astype(np.float64)
+        assert np.array_equal(y, w.astype(np.float64).T[:m]), "one-hot m=%d" % m
+    y = q4.q4_gemm_f16(gpu(np.zeros((300, k), np.float16)), wg)
+    assert bool(torch.all(y == 0))
+    y = q4.q4_gemm_f16(gpu(rng.standard_normal((20, k)).astype(np.float16)),
+                       gpu(np.zeros((n, k), np.float16)))
+    assert bool(torch.all(y == 0))
+
+
+def test_gemm_f16_deterministic_small_m_and_binding_errors(q4):
+    x, w = _f16_case(300, 999, 2560, seed=8)
+    xg, wg = gpu(x), gpu(w)
+    a = q4.q4_gemm_f16(xg, wg)
+    b = q4.q4_gemm_f16(xg, wg)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    # m <= 8 is the decode kernel, bit for bit
+    for m in (1, 8):
+        assert torch.equal(q4.q4_gemm_f16(xg[:m], wg), q4.q4_gemv_f16(xg[:m], wg))
+    with pytest.raises(ValueError):
+        q4.q4_gemm_f16(gpu(np.zeros((9, 64), np.float16)), gpu(np.zeros((4, 32), np.float16)))
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemm_f16(gpu(np.zeros((9, 48), np.float16)), gpu(np.zeros((4, 48), np.float16)))
+
+
+@pytest.mark.parametrize("m", [512, 2048])
+def test_gemm_f16_prefill_full_size(q4, orc, m):
+    """The 4B prefill projection (K=2560, N=4096) with fp16 weights at full size:
+    sampled columns against the oracle on every token."""
+    mat = qi.PREFILL_4B
+    _log("f16 gemm %s m=%d n=%d k=%d: generating" % (mat.name, m, mat.n, mat.k))
+    w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id).astype(np.float16)
+    x = qi.activations(m, mat.k, outliers=True)
+    y = q4.q4_gemm_f16(gpu(x), gpu(w))
+    torch.cuda.synchronize()
+    rows = _sample_rows(mat.n, np.random.default_rng(mat.tensor_id), count=128)
+    y_ref, bound = orc.matmul_f16(x, w[rows])
+    gy = y.cpu().numpy().astype(np.float64)[:, rows]
+    assert_within(gy, y_ref, bound, "f16 gemm %s m=%d" % (mat.name, m))
+
+
+# --------------------------------------------------------------------------
 # the five workload configurations at full size, compared on sampled rows
 # --------------------------------------------------------------------------
 
