@@ -13,7 +13,7 @@
 // 16x16 D layout a lane's four values share one column, hence one scale.
 //
 // Work split.  A workgroup (4 or 8 waves: one or two per SIMD) owns a
-// BM x (32*WN) tile of y.  Its waves are WN column slices of 32 x WK slices of K: each wave covers
+// BM x (32*WN) tile of y (WN = 1, 2 or 4).  Its waves are WN column slices of 32 x WK slices of K: each wave covers
 // all BM rows and 32 columns over G/WK groups, so every code is unpacked by
 // exactly one wave and every activation is read from LDS by WN waves.  The
 // WK partial tiles are added in LDS at the end in a fixed order
@@ -24,6 +24,7 @@
 //   activations  16 rows x 64 bytes of one group per wave instruction (1 KiB);
 //                each lane reads its A operand with one ds_read_b128
 //   codes        one whole 16-byte group of 64 columns per instruction
+//                (two instructions per group for 128-column tiles)
 //   scales       one fp16 per column, each landing in a 4-byte LDS slot
 // so the loop body issues no register-destination global loads and the only
 // waits on global memory are the explicit per-stage vmcnt waits below.
@@ -50,17 +51,20 @@ template <int BM, int WN, int WK, int KG, int S>
 struct Gemm {
     static constexpr int MB = BM / 16;                     // 16-row blocks per wave
     static constexpr int BN = 32 * WN;
+    static constexpr int H = (BN + 63) / 64;                         // 64-column code blocks
     static constexpr int kCodeOff = KG * MB * kBlockBytes;           // within a stage
-    static constexpr int kScaleOff = kCodeOff + KG * kBlockBytes;
-    static constexpr int kStageBytes = kScaleOff + KG * 256;         // per K slice
+    static constexpr int kScaleOff = kCodeOff + KG * H * kBlockBytes;
+    static constexpr int kStageBytes = kScaleOff + KG * H * 256;     // per K slice
     static constexpr int kABlocksPerWave = KG * MB / WN;
-    // codes + scales of group gl are loaded by wave gl % WN of the K slice
-    static constexpr int groups_of(int wn) { return (KG - wn + WN - 1) / WN; }
+    // codes + scales of item i = (group i / H, 64-column block i % H) are
+    // loaded by wave i % WN of the K slice
+    static constexpr int groups_of(int wn) { return (KG * H - wn + WN - 1) / WN; }
     static constexpr int loads_per_stage(int wn) { return kABlocksPerWave + 2 * groups_of(wn); }
     static constexpr int kLdsBytes = WK * S * kStageBytes;
     static constexpr int kRedBytes = (WK - 1) * WN * MB * 8 * 64 * 4;
     static constexpr int kThreads = 64 * WN * WK;
     static_assert(WN * WK == 4 || WN * WK == 8, "one or two waves per SIMD");
+    static_assert(WN <= 4 && H <= 2, "at most four column slices (128 columns)");
     static_assert((KG * MB) % WN == 0, "activation blocks split evenly");
     static_assert(S >= 2, "at least double buffering");
     static_assert(kRedBytes <= kLdsBytes, "reduction fits in the staging space");
@@ -132,9 +136,14 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
 
     // load-side lane mappings
     const int a_row = lane >> 2, a_part = lane & 3;       // 16 rows x 4 16-byte parts
-    const int64_t ld_col = min<int64_t>(nt0 + lane, N - 1);   // codes / scales: lane = column
-    const uint8_t* code_row = packed + ld_col * (K / 2);
-    const uint16_t* scale_row = scales + ld_col * G;
+    // codes / scales: lane = column of a 64-column block (two scalar pointers:
+    // a local array of pointers here made the compiler drop the kernel's host stub)
+    const int64_t ld_col0 = min<int64_t>(nt0 + lane, N - 1);
+    const int64_t ld_col1 = min<int64_t>(nt0 + 64 + lane, N - 1);
+    const uint8_t* code_row0 = packed + ld_col0 * (K / 2);
+    const uint8_t* code_row1 = packed + ld_col1 * (K / 2);
+    const uint16_t* scale_row0 = scales + ld_col0 * G;
+    const uint16_t* scale_row1 = scales + ld_col1 * G;
     // operand-side lane mapping
     const int col = lane & 15, kq = lane >> 4;
 
@@ -152,14 +161,15 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
                                              16, 0, 0);
         }
 #pragma unroll
-        for (int gl = 0; gl < KG; ++gl) {
-            if (gl % WN != wn) continue;
+        for (int it = 0; it < KG * C::H; ++it) {
+            if (it % WN != wn) continue;
+            const int gl = it / C::H, h = it % C::H;
             const int g = min(gs + gl, G - 1);
-            __builtin_amdgcn_global_load_lds(code_row + 16 * g,
-                                             (lds_void_t*)(sb + C::kCodeOff + gl * kBlockBytes),
+            __builtin_amdgcn_global_load_lds((h ? code_row1 : code_row0) + 16 * g,
+                                             (lds_void_t*)(sb + C::kCodeOff + it * kBlockBytes),
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds(scale_row + g,
-                                             (lds_void_t*)(sb + C::kScaleOff + gl * 256), 2, 0,
+            __builtin_amdgcn_global_load_lds((h ? scale_row1 : scale_row0) + g,
+                                             (lds_void_t*)(sb + C::kScaleOff + it * 256), 2, 0,
                                              0);
         }
     };
@@ -192,9 +202,10 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int c = 32 * wn + 16 * nb + col;
-            o.code[nb] = *reinterpret_cast<const uint32_t*>(sb + C::kCodeOff + gl * kBlockBytes +
-                                                            16 * c + 4 * kq);
-            o.sc[nb] = *reinterpret_cast<const _Float16*>(sb + C::kScaleOff + gl * 256 + 4 * c);
+            o.code[nb] = *reinterpret_cast<const uint32_t*>(
+                sb + C::kCodeOff + gl * C::H * kBlockBytes + 16 * c + 4 * kq);
+            o.sc[nb] = *reinterpret_cast<const _Float16*>(sb + C::kScaleOff + gl * C::H * 256 +
+                                                          4 * c);
         }
     };
     auto compute = [&](const Ops& o) {
@@ -232,8 +243,10 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(0) * (S - 2)));
                 else if (wn == 1)
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(1) * (S - 2)));
+                else if (wn == 2)
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(2) * (S - 2)));
                 else
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(WN - 1) * (S - 2)));
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(3) * (S - 2)));
                 barrier_keep_loads();
                 // refill the buffer computed last iteration (every wave is past it)
                 issue(st + S - 1, (u + S - 1) % S);
@@ -326,7 +339,11 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
         return launch_gemm_t<32, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
     if (m < 256)
         return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
-    return launch_gemm_t<128, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+    if (m < 1024)
+        return launch_gemm_t<128, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+    // from 1024 rows on, 128 x 128 tiles still give every CU a tile and halve
+    // the activation traffic per output (measured 15% faster at M = 2048)
+    return launch_gemm_t<128, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
 }
 
 }  // namespace

@@ -240,7 +240,13 @@ hipError_t launch_gemm_f16(const uint16_t* x, const uint16_t* w, float* y, int64
     if (m <= 16) return launch_gemm_f16_t<16, 1, 4, 2, 4>(x, w, y, m, n, k, stream);
     if (m <= 32) return launch_gemm_f16_t<32, 1, 4, 2, 4>(x, w, y, m, n, k, stream);
     if (m < 256) return launch_gemm_f16_t<64, 2, 4, 2, 2>(x, w, y, m, n, k, stream);
-    return launch_gemm_f16_t<128, 2, 4, 1, 3>(x, w, y, m, n, k, stream);
+    if (m < 512) return launch_gemm_f16_t<128, 2, 4, 1, 3>(x, w, y, m, n, k, stream);
+    // wider tiles without a K split once every CU still gets one: with 3.6x
+    // the weight bytes of Q4, fewer weight re-reads per output pay (measured
+    // at K = 2560, N = 4096: 28.1 against 34.5 us at M = 512, 96.7 against
+    // 126 us at M = 2048)
+    if (m < 1024) return launch_gemm_f16_t<64, 4, 1, 2, 4>(x, w, y, m, n, k, stream);
+    return launch_gemm_f16_t<128, 4, 1, 1, 8>(x, w, y, m, n, k, stream);
 }
 
 }  // namespace q4

@@ -139,7 +139,7 @@ def test_single_token_streaming(q4, orc, n, k):
     assert_within(y, y_ref, bound, "q4_gemv m=1 n=%d k=%d" % (n, k))
 
 
-@pytest.mark.parametrize("m", [9, 15, 16, 17, 31, 64, 100, 128, 129, 300])
+@pytest.mark.parametrize("m", [9, 15, 16, 17, 31, 64, 100, 128, 129, 300, 1024, 1100])
 @pytest.mark.parametrize("n,k", [(17, 96), (64, 256), (130, 2560), (200, 160), (70, 1056)])
 def test_prefill_product(q4, orc, m, n, k):
     x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m * 31 + n * 7 + k)
@@ -266,6 +266,7 @@ GEMM_MULTI_SETS = [
     (128, 2560, (130, 5, 257, 64)),
     (300, 96, (17, 200, 3, 1, 70, 33, 9, 129)),            # eight matrices
     (512, 1024, (100, 61)),
+    (1030, 256, (130, 61, 257)),                           # 128 x 128 tiles
     (3, 256, (15, 100)),                                   # m <= 8: the q4_gemv_multi path
 ]
 
@@ -522,7 +523,7 @@ F16_GEMM_SHAPES = [(15, 64), (17, 96), (100, 1056), (257, 2560), (61, 4096), (10
 
 
 @pytest.mark.parametrize("n,k", F16_GEMM_SHAPES)
-@pytest.mark.parametrize("m", [9, 16, 17, 32, 33, 64, 100, 255, 256, 300])
+@pytest.mark.parametrize("m", [9, 16, 17, 32, 33, 64, 100, 255, 256, 300, 520, 1030])
 def test_gemm_f16_product(q4, orc, m, n, k):
     x, w = _f16_case(m, n, k, seed=m * 11 + n + 3 * k)
     _log("q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
