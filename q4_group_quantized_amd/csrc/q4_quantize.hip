@@ -8,12 +8,24 @@
 // the ones the public header q4.h states; the result is unique, so this kernel
 // must agree bit for bit with any other correct implementation.
 //
-// Mapping: 8 lanes per group, each lane owns 4 consecutive fp32 weights (one
-// 16-byte load), so a wave reads 8 groups = 1 KiB of contiguous weights per
-// load.  The group maximum is reduced over the 8 lanes with DPP-class lane
-// exchanges; every lane then derives the same scale and quantizes its four
-// weights.  Stores: 2 packed bytes per lane (128 contiguous bytes per wave)
-// and one scale per group.
+// Mapping: 4 lanes per group, each lane owns 8 consecutive fp32 weights (two
+// 16-byte loads), so a wave covers 16 groups = 2 KiB of contiguous weights
+// per step.  Every wave walks its own contiguous range of steps front to back
+// with PF steps of loads in flight (refills past the range re-read its last
+// step, so every load is unconditional).  The group maximum is reduced over
+// the 4 lanes with DPP quad permutes; every lane then derives the same scale.
+// Stores: 4 packed bytes per lane (256 contiguous bytes per wave) and one
+// scale per group.
+//
+// Levels without a division per weight.  With r = 1/s (IEEE fp32), the
+// product t = w * r differs from the IEEE quotient fl(w / s) by less than
+// |w / s| * 2^-22 <= 2.6e-6, because |w / s| <= 10.5 (s is max|w|/7 rounded to
+// binary16, at worst 1.5x too small in the subnormal range).  rne(t) and
+// rne(fl(w / s)) can therefore only differ when t lies within that distance of
+// a half-integer; for those weights (|t - rne(t)| >= 0.5 - 4e-6, about one in
+// 10^5 for spread data) the level is taken from the IEEE quotient itself, so
+// the result is bit-identical to dividing every weight.  s = 0 gives level 0
+// by the rule; s = inf gives r = 0, the same levels as the quotient w / inf.
 //
 // Numerics: fp32 division is IEEE correctly rounded (hipcc default; this code
 // must never be built with fast-math or approximate-division flags), fp32 and
@@ -25,57 +37,99 @@
 namespace q4 {
 namespace {
 
-constexpr int kQuantThreads = 256;
-constexpr int kLanesPerGroup = 8;
-constexpr int kGroupsPerBlock = kQuantThreads / kLanesPerGroup;
+constexpr int kQuantWaves = 4;
+constexpr int kQuantThreads = 64 * kQuantWaves;
+constexpr int kGroupsPerStep = 16;          // per wave
+constexpr int kQuantPrefetch = 4;           // steps in flight per wave
+constexpr int kQuantWavesPerSimd = 2;
 
-__device__ __forceinline__ int level_of(float w, float s) {
-    float v = rintf(w / s);
-    v = fminf(fmaxf(v, -8.0f), 7.0f);
-    return s == 0.0f ? 0 : (int)v;
+struct QuantStep {
+    f32x4_t a, b;                           // weights 8 sub .. 8 sub + 7 of the group
+};
+
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                               __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                               __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    return v;
 }
 
+// code (level + 8) of weight v for scale s (> 0 or inf) with r = 1/s
+__device__ __forceinline__ uint32_t code_of(float v, float s, float r) {
+    const float t = v * r;
+    float n = rintf(t);
+    if (fabsf(t - n) >= 0.5f - 4e-6f) n = rintf(v / s);   // near a midpoint: the IEEE quotient
+    n = fminf(fmaxf(n, -8.0f), 7.0f);
+    return (uint32_t)((int)n + 8);
+}
+
+// Wave w owns steps [w * base + min(w, extra), + base + (w < extra)); step f
+// covers groups 16 f .. 16 f + 15 (the last step may run past ngroups: those
+// lanes load the last group and store nothing).
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     const float* __restrict__ w, uint8_t* __restrict__ packed,
-    uint16_t* __restrict__ scales, int64_t ngroups) {
-    const int sub = threadIdx.x & (kLanesPerGroup - 1);
-    const int64_t stride = (int64_t)gridDim.x * kGroupsPerBlock;
-    // The loop bound is uniform per block so that all lanes of a group take
-    // part in the lane exchange together.
-    for (int64_t base = (int64_t)blockIdx.x * kGroupsPerBlock; base < ngroups;
-         base += stride) {
-        const int64_t g = base + (threadIdx.x / kLanesPerGroup);
-        const bool live = g < ngroups;
-        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-        if (live)
-            v = __builtin_nontemporal_load(
-                reinterpret_cast<const f32x4_t*>(w + g * 32 + sub * 4));
-        float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])),
-                           fmaxf(fabsf(v[2]), fabsf(v[3])));
-        amax = fmaxf(amax, __shfl_xor(amax, 1, kLanesPerGroup));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, kLanesPerGroup));
-        amax = fmaxf(amax, __shfl_xor(amax, 4, kLanesPerGroup));
+    uint16_t* __restrict__ scales, int64_t ngroups, int64_t base, int64_t extra) {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 3;
+    const int gi = lane >> 2;
+    const int64_t wv = (int64_t)blockIdx.x * kQuantWaves +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t s0 = wv * base + (wv < extra ? wv : extra);
+    const int64_t cnt = base + (wv < extra ? 1 : 0);
+    if (cnt <= 0) return;
 
-        const float ratio = amax / 7.0f;                    // IEEE fp32 division
-        const _Float16 s16 = (_Float16)ratio;               // round to nearest even
+    auto load = [&](QuantStep& q, int64_t f) {
+        int64_t g = (s0 + (f < cnt ? f : cnt - 1)) * kGroupsPerStep + gi;
+        g = g < ngroups ? g : ngroups - 1;
+        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(w + g * 32 + sub * 8);
+        q.a = __builtin_nontemporal_load(p);
+        q.b = __builtin_nontemporal_load(p + 1);
+    };
+    auto quantize_step = [&](const QuantStep& q, int64_t f) {
+        float amax = fmaxf(fmaxf(fmaxf(fabsf(q.a[0]), fabsf(q.a[1])),
+                                 fmaxf(fabsf(q.a[2]), fabsf(q.a[3]))),
+                           fmaxf(fmaxf(fabsf(q.b[0]), fabsf(q.b[1])),
+                                 fmaxf(fabsf(q.b[2]), fabsf(q.b[3]))));
+        amax = quad_max(amax);
+        const float ratio = amax / 7.0f;                 // IEEE fp32 division
+        const _Float16 s16 = (_Float16)ratio;            // round to nearest even
         const float s = (float)s16;
+        const float r = 1.0f / s;                        // IEEE fp32 division
+        uint32_t word = 0x88888888u;                     // level 0 everywhere (s == 0)
+        if (s != 0.0f) {
+            word = code_of(q.a[0], s, r) | (code_of(q.a[1], s, r) << 4) |
+                   (code_of(q.a[2], s, r) << 8) | (code_of(q.a[3], s, r) << 12) |
+                   (code_of(q.b[0], s, r) << 16) | (code_of(q.b[1], s, r) << 20) |
+                   (code_of(q.b[2], s, r) << 24) | (code_of(q.b[3], s, r) << 28);
+        }
+        const int64_t g = (s0 + f) * kGroupsPerStep + gi;
+        if (g < ngroups) {
+            reinterpret_cast<uint32_t*>(packed + g * 16)[sub] = word;
+            if (sub == 0) scales[g] = __builtin_bit_cast(uint16_t, s16);
+        }
+    };
 
-        const int q0 = level_of(v[0], s) + 8;
-        const int q1 = level_of(v[1], s) + 8;
-        const int q2 = level_of(v[2], s) + 8;
-        const int q3 = level_of(v[3], s) + 8;
-        const uint16_t two_bytes =
-            (uint16_t)((q0 | (q1 << 4)) | ((q2 | (q3 << 4)) << 8));
-        if (live) {
-            reinterpret_cast<uint16_t*>(packed + g * 16)[sub] = two_bytes;
-            if (sub == 0)
-                scales[g] = __builtin_bit_cast(uint16_t, s16);
+    QuantStep ring[kQuantPrefetch];
+#pragma unroll
+    for (int p = 0; p < kQuantPrefetch; ++p) load(ring[p], p);
+    int64_t f0 = 0;
+    for (; f0 + kQuantPrefetch < cnt; f0 += kQuantPrefetch) {
+#pragma unroll
+        for (int p = 0; p < kQuantPrefetch; ++p) {
+            const QuantStep q = ring[p];
+            load(ring[p], f0 + p + kQuantPrefetch);
+            quantize_step(q, f0 + p);
         }
     }
+#pragma unroll
+    for (int p = 0; p < kQuantPrefetch; ++p)
+        if (f0 + p < cnt) quantize_step(ring[p], f0 + p);
 }
 
 }  // namespace
 
+// Two waves per SIMD, each with a contiguous, balanced range of 16-group steps.
 hipError_t launch_quantize(const float* w, uint8_t* packed, uint16_t* scales,
                            int64_t n, int64_t k, hipStream_t stream) {
     const int64_t ngroups = n * (k / 32);
@@ -83,11 +137,15 @@ hipError_t launch_quantize(const float* w, uint8_t* packed, uint16_t* scales,
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return e;
-    const int64_t want = (ngroups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-    const int64_t cap = (int64_t)device_info(dev).cu_count * 16;
-    const int blocks = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(kQuantThreads), 0,
-                       stream, w, packed, scales, ngroups);
+    const int64_t steps = (ngroups + kGroupsPerStep - 1) / kGroupsPerStep;
+    const int64_t max_waves =
+        (int64_t)device_info(dev).cu_count * kQuantWaves * kQuantWavesPerSimd;
+    const int64_t per = (steps + max_waves - 1) / max_waves;
+    const int64_t waves = (steps + per - 1) / per;
+    const int blocks = (int)((waves + kQuantWaves - 1) / kQuantWaves);
+    const int64_t W = (int64_t)blocks * kQuantWaves;
+    hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, w,
+                       packed, scales, ngroups, steps / W, steps % W);
     return hipGetLastError();
 }
 

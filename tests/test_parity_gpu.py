@@ -100,6 +100,20 @@ def test_quantize_bit_exact(q4, orc, n, k):
     assert np.array_equal(packed, rp), np.argwhere(packed != rp)[:5]
 
 
+def test_quantize_midpoints_everywhere(q4, orc):
+    """Every group a tie group (weights on level midpoints and one ulp either
+    side, normal and subnormal scales): the kernel's midpoint fallback runs in
+    many lanes of many waves at once."""
+    rng = np.random.default_rng(2024)
+    n, k = 256, 1024
+    w = oracle_pins._tie_groups(rng, n * k // 32).reshape(n, k)
+    _log("quantize midpoints n=%d k=%d" % (n, k))
+    packed, scales = gpu_quantize(q4, w)
+    rp, rs = orc.quantize(w)
+    assert np.array_equal(scales, rs), np.argwhere(scales != rs)[:5]
+    assert np.array_equal(packed, rp), np.argwhere(packed != rp)[:5]
+
+
 # --------------------------------------------------------------------------
 # products on small shapes, compared in full
 # --------------------------------------------------------------------------
