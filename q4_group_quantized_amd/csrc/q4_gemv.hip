@@ -188,7 +188,11 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
     const int T = ((G + 7) & ~7) / kTileGroups;          // tiles per row block
     const int64_t F = count * T;                         // flat steps of this wave
 
-    // load cursor; steps past the wave's range re-read row N-1 (see load_tile)
+    // load cursor, advanced with selects rather than branches: with a
+    // branch-free loop body the compiler keeps the later tiles' loads in
+    // flight instead of waiting for every load at each tile (measured 7%
+    // faster on the M = 8 LM head).  Steps past the wave's range re-read row
+    // N-1 (see load_tile).
     const int64_t rb_end = rb_begin + count;
     int64_t lrb = rb_begin;
     int lt = 0;
@@ -197,7 +201,10 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
         const int64_t nc = (lrb < rb_end && n < N) ? n : N - 1;
         Tile t = load_tile<kScale16>(packed + nc * (int64_t)(K / 2), scales + nc * (int64_t)G,
                                      lt * kTileGroups, kb, G);
-        if (++lt == T) { lt = 0; ++lrb; }
+        const int nt = lt + 1;
+        const bool wrap = nt == T;
+        lt = wrap ? 0 : nt;
+        lrb += wrap ? 1 : 0;
         return t;
     };
 
@@ -215,19 +222,30 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
     int64_t crb = rb_begin;
     int ct = 0;
     const int cg = T * kTileGroups;
-    for (int64_t f0 = 0; f0 < F; f0 += kPrefetch) {
+    auto finish = [&]() {                       // after each tile: store a finished row block
+        if (++ct == T) {
+            store_rows<TB>(y, acc, crb, lane, M, N);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[tb] = 0.f;
+            ct = 0;
+            ++crb;
+        }
+    };
+    // full rounds of kPrefetch tiles, then the last tiles with no new loads
+    int64_t f0 = 0;
+    for (; f0 + kPrefetch < F; f0 += kPrefetch) {
 #pragma unroll
         for (int p = 0; p < kPrefetch; ++p) {
-            if (f0 + p < F)
-                compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, a, acc);
+            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, a, acc);
             ring[p] = load_next();
-            if (f0 + p < F && ++ct == T) {
-                store_rows<TB>(y, acc, crb, lane, M, N);
+            finish();
+        }
+    }
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) acc[tb] = 0.f;
-                ct = 0;
-                ++crb;
-            }
+    for (int p = 0; p < kPrefetch; ++p) {
+        if (f0 + p < F) {
+            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, a, acc);
+            finish();
         }
     }
 }
