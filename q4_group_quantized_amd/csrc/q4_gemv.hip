@@ -563,17 +563,12 @@ constexpr int gemv1_prefetch(int gpl) {
     return gpl <= 1 ? 8 : gpl == 2 ? 4 : gpl == 3 ? 3 : 2;
 }
 constexpr int gemv1_waves_per_simd(int gpl) { return gpl <= 3 ? 2 : 1; }
-// The top-k variant (more work per step, LDS buffers) keeps one wave per SIMD
-// with about 16 code loads per lane in flight.
-constexpr int gemv1_topk_prefetch(int gpl) {
-    return gpl <= 2 ? 8 : gpl == 3 ? 6 : gpl <= 5 ? 4 : gpl <= 7 ? 3 : 2;
-}
 
 template <int LPR, int GPL>
 hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* const* packed,
                           const uint16_t* const* scales, float* const* y, const int64_t* n,
                           uint64_t* partials, hipStream_t stream) {
-    constexpr int PF = gemv1_prefetch(GPL), PFT = gemv1_topk_prefetch(GPL);
+    constexpr int PF = gemv1_prefetch(GPL);
     constexpr int RPS = 64 / LPR;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -582,7 +577,7 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
     seg.count = count;
     int64_t total_rq = 0;
     for (int s = 0; s < count; ++s) total_rq += (n[s] + RPS - 1) / RPS;
-    const int wps = partials ? 1 : gemv1_waves_per_simd(GPL);
+    const int wps = gemv1_waves_per_simd(GPL);
     const int64_t max_waves = (int64_t)device_info(dev).cu_count * kGemvWaves * wps;
     const int64_t per = (total_rq + max_waves - 1) / max_waves;   // steps per wave
     int64_t wave0 = 0;
@@ -601,7 +596,7 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
     }
     const int blocks = (int)((wave0 + kGemvWaves - 1) / kGemvWaves);
     if (partials)
-        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PFT, true>), dim3(blocks), dim3(kGemvThreads),
+        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, true>), dim3(blocks), dim3(kGemvThreads),
                            0, stream, x, k, seg, kSpliceConsts, partials);
     else
         hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, false>), dim3(blocks), dim3(kGemvThreads),
@@ -666,12 +661,13 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed,
 }
 
 int64_t gemv1_topk_lists(int64_t n, int64_t k, int cu_count) {
-    if (gemv1_lanes_per_row(k) == 0) return 0;
-    // the m = 1 launcher's grid for one matrix of n rows in its top-k form: at
-    // most one wave per SIMD, rounded up to whole workgroups
     const int lpr = gemv1_lanes_per_row(k);
+    if (lpr == 0) return 0;
+    // the m = 1 launcher's grid for one matrix of n rows (launch_gemv1_t):
+    // waves per SIMD from the groups per lane, rounded up to whole workgroups
+    const int gpl = (int)((k / 32) / lpr);
     const int64_t rq = (n + 64 / lpr - 1) / (64 / lpr);
-    const int64_t max_waves = (int64_t)cu_count * kGemvWaves;
+    const int64_t max_waves = (int64_t)cu_count * kGemvWaves * gemv1_waves_per_simd(gpl);
     const int64_t per = (rq + max_waves - 1) / max_waves;
     const int64_t waves = (rq + per - 1) / per;
     return (waves + kGemvWaves - 1) / kGemvWaves;            // one list per workgroup
