@@ -1,5 +1,6 @@
 // q4_gemv_f16.hip -- decode-time product with fp16 weights on gfx950:
-// y[m, n] = sum_k x[m, k] * w[n, k] for 1 <= m <= 8.
+// y[m, n] = sum_k x[m, k] * w[n, k] for 1 <= m <= 8 (m = 1 has a streaming
+// kernel of its own, below the MFMA kernel).
 //
 // Method: the F16 GEMV of the QORA engines, their second weight format beside
 // Q4 (QORA-4B article, quantization section, format table; QORA-LLM-0.8B
@@ -116,14 +117,152 @@ __global__ __launch_bounds__(kF16Threads, 1) void gemv_f16_kernel(
         if (f0 + p < F) compute(ring[p]);
 }
 
+// m = 1: a streaming kernel without the matrix core.  LPR lanes share a row
+// (RPS = 64 / LPR rows per wave step) and lane `sub` owns the 16-byte chunks
+// at byte offsets 16 sub + 16 LPR i (i < CPL) of every row, so one wave load
+// covers RPS rows x 16 LPR contiguous bytes and the lane's CPL activation
+// chunks stay in registers for the whole kernel.  Per chunk: four
+// v_dot2_f32_f16 (exact fp16 products, fp32 sums); the LPR partial sums of a
+// row are added with DPP rotations.  Each wave walks its own contiguous range
+// of rows with PF steps of loads in flight, refills past the range re-reading
+// its last step.  (The MFMA kernel reads 16 rows x 64 bytes per wave load,
+// which streams at ~5.3 TB/s; this layout streams at 6.6-6.9 TB/s.)
+constexpr int kF16m1Prefetch = 2;
+
+template <int LPR>
+__device__ __forceinline__ float f16_lanes_sum(float v) {
+    v = row16_sum(v);
+    if (LPR >= 32) v += __shfl_xor(v, 16, 64);
+    if (LPR == 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+template <int LPR, int CPL, int PF>
+__global__ __launch_bounds__(kF16Threads) void gemv_f16_m1_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ y,
+    int64_t N, int K, int64_t base, int64_t extra) {
+    constexpr int RPS = 64 / LPR;
+    const int lane = threadIdx.x & 63, sub = lane % LPR, r = lane / LPR;
+    const int64_t wv = (int64_t)blockIdx.x * kF16Waves +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t q0 = wv * base + (wv < extra ? wv : extra);
+    const int64_t cnt = base + (wv < extra ? 1 : 0);
+    if (cnt <= 0) return;
+    const int64_t row0 = RPS * q0 + r;
+    u32x4_t rp[PF][CPL];
+    auto load = [&](int slot, int64_t f) {
+        int64_t row = row0 + RPS * (f < cnt ? f : cnt - 1);
+        row = row < N ? row : N - 1;                 // the last step may be partial
+        const uint16_t* p = w + row * (int64_t)K + 8 * sub;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            rp[slot][i] =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 8 * LPR * i));
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load(p, p);
+    u32x4_t xr[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        xr[i] = *reinterpret_cast<const u32x4_t*>(x + 8 * sub + 8 * LPR * i);
+    auto compute = [&](int p) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            a0 = __builtin_amdgcn_fdot2(as_half2(rp[p][i][0]), as_half2(xr[i][0]), a0, false);
+            a1 = __builtin_amdgcn_fdot2(as_half2(rp[p][i][1]), as_half2(xr[i][1]), a1, false);
+            a0 = __builtin_amdgcn_fdot2(as_half2(rp[p][i][2]), as_half2(xr[i][2]), a0, false);
+            a1 = __builtin_amdgcn_fdot2(as_half2(rp[p][i][3]), as_half2(xr[i][3]), a1, false);
+        }
+        return f16_lanes_sum<LPR>(a0 + a1);
+    };
+    auto emit = [&](float acc, int64_t f) {
+        const int64_t row = row0 + RPS * f;
+        if (sub == 0 && row < N) y[row] = acc;
+    };
+    int64_t f0 = 0;
+    for (; f0 + PF < cnt; f0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const float acc = compute(p);
+            load(p, f0 + p + PF);
+            emit(acc, f0 + p);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (f0 + p < cnt) emit(compute(p), f0 + p);
+}
+
+template <int LPR, int CPL>
+hipError_t launch_f16_m1_t(const uint16_t* x, const uint16_t* w, float* y, int64_t n, int64_t k,
+                           int cu, hipStream_t stream) {
+    constexpr int RPS = 64 / LPR;
+    const int64_t rq = (n + RPS - 1) / RPS;                  // row steps
+    const int64_t max_waves = (int64_t)cu * kF16Waves;       // one wave per SIMD
+    const int64_t per = (rq + max_waves - 1) / max_waves;
+    const int64_t waves = (rq + per - 1) / per;
+    const int blocks = (int)((waves + kF16Waves - 1) / kF16Waves);
+    const int64_t W = (int64_t)blocks * kF16Waves;
+    hipLaunchKernelGGL((gemv_f16_m1_kernel<LPR, CPL, kF16m1Prefetch>), dim3(blocks),
+                       dim3(kF16Threads), 0, stream, x, w, y, n, (int)k, rq / W, rq % W);
+    return hipGetLastError();
+}
+
+// The m = 1 configuration for k (k = 16 LPR CPL), or false when k has none.
+hipError_t launch_f16_m1(const uint16_t* x, const uint16_t* w, float* y, int64_t n, int64_t k,
+                         int cu, hipStream_t stream, bool& done) {
+    done = true;
+    if (k % 128 == 0 && k / 128 <= 8) {
+        switch (k / 128) {
+            case 1: return launch_f16_m1_t<16, 1>(x, w, y, n, k, cu, stream);
+            case 2: return launch_f16_m1_t<16, 2>(x, w, y, n, k, cu, stream);
+            case 3: return launch_f16_m1_t<16, 3>(x, w, y, n, k, cu, stream);
+            case 4: return launch_f16_m1_t<16, 4>(x, w, y, n, k, cu, stream);
+            case 5: return launch_f16_m1_t<16, 5>(x, w, y, n, k, cu, stream);
+            case 6: return launch_f16_m1_t<16, 6>(x, w, y, n, k, cu, stream);
+            case 7: return launch_f16_m1_t<16, 7>(x, w, y, n, k, cu, stream);
+            default: return launch_f16_m1_t<16, 8>(x, w, y, n, k, cu, stream);
+        }
+    }
+    if (k % 256 == 0 && k / 256 <= 10) {
+        switch (k / 256) {
+            case 5: return launch_f16_m1_t<32, 5>(x, w, y, n, k, cu, stream);
+            case 6: return launch_f16_m1_t<32, 6>(x, w, y, n, k, cu, stream);
+            case 7: return launch_f16_m1_t<32, 7>(x, w, y, n, k, cu, stream);
+            case 8: return launch_f16_m1_t<32, 8>(x, w, y, n, k, cu, stream);
+            case 9: return launch_f16_m1_t<32, 9>(x, w, y, n, k, cu, stream);
+            default: return launch_f16_m1_t<32, 10>(x, w, y, n, k, cu, stream);
+        }
+    }
+    if (k % 512 == 0 && k / 512 >= 6 && k / 512 <= 10) {
+        switch (k / 512) {
+            case 6: return launch_f16_m1_t<64, 6>(x, w, y, n, k, cu, stream);
+            case 7: return launch_f16_m1_t<64, 7>(x, w, y, n, k, cu, stream);
+            case 8: return launch_f16_m1_t<64, 8>(x, w, y, n, k, cu, stream);
+            case 9: return launch_f16_m1_t<64, 9>(x, w, y, n, k, cu, stream);
+            default: return launch_f16_m1_t<64, 10>(x, w, y, n, k, cu, stream);
+        }
+    }
+    done = false;
+    return hipSuccess;
+}
+
 }  // namespace
 
-// One wave per SIMD, each with a contiguous, balanced range of row blocks.
+// m = 1: the streaming kernel where k fits it; otherwise (and for m = 2..8)
+// the MFMA kernel, one wave per SIMD, each with a contiguous, balanced range
+// of row blocks.
 hipError_t launch_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
                            int64_t n, int64_t k, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    if (m == 1) {
+        bool done = false;
+        e = launch_f16_m1(x, w, y, n, k, device_info(dev).cu_count, stream, done);
+        if (done) return e;
+    }
     const int64_t RB = (n + 15) / 16;
     const int64_t max_waves = (int64_t)device_info(dev).cu_count * kF16Waves;
     const int64_t per = (RB + max_waves - 1) / max_waves;

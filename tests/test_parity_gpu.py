@@ -501,6 +501,22 @@ def test_gemv_f16_exact_special_inputs(q4):
     assert bool(torch.all(y == 0))
 
 
+@pytest.mark.parametrize("k", [256, 2560, 4096])
+def test_gemv_f16_single_token_one_hot(q4, k):
+    """m = 1 streaming path (16, 32 and 64 lanes per row): a one-hot x picks one
+    weight column exactly, for every position in a lane's chunks."""
+    rng = np.random.default_rng(k)
+    n = 70
+    w = rng.standard_normal((n, k)).astype(np.float16)
+    wg = gpu(w)
+    _log("q4_gemv_f16 m=1 one-hot k=%d" % k)
+    for e in list(range(0, 24)) + list(range(k - 24, k)) + list(rng.integers(0, k, 16)):
+        x = np.zeros((1, k), np.float16)
+        x[0, e] = 1.0
+        y = q4.q4_gemv_f16(gpu(x), wg).cpu().numpy().astype(np.float64)
+        assert np.array_equal(y[0], w[:, e].astype(np.float64)), "one-hot position %d" % e
+
+
 def test_gemv_f16_deterministic_and_binding_errors(q4):
     x, w = _f16_case(8, 999, 2560, seed=6)
     xg, wg = gpu(x), gpu(w)
