@@ -149,13 +149,13 @@ def traffic_record(fetch_csv: str, write_csv: str) -> None:
     traffic = g_fetch * 1024.0 * f_fetch + g_write * 1024.0 * f_write
     lines = [
         "# HBM traffic of one q4_gemv launch on the 0.8B LM head (m=1, n=%d, k=%d)" % (mat.n, mat.k),
-        "# Commands (repository root on the GPU host; one counter per run):",
-        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmcf "
+        "# Commands (REPO = the repository root, OUT = any output directory; one counter per run):",
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $OUT/pmcf "
         "-o f --output-format csv -- python3 $REPO/bench.py --traffic-probe",
-        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmcw "
+        "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $OUT/pmcw "
         "-o w --output-format csv -- python3 $REPO/bench.py --traffic-probe",
-        "#   python3 bench.py --traffic-record gpurun_out/pmcf/f_counter_collection.csv "
-        "gpurun_out/pmcw/w_counter_collection.csv",
+        "#   python3 bench.py --traffic-record $OUT/pmcf/f_counter_collection.csv "
+        "$OUT/pmcw/w_counter_collection.csv",
         "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the probe's launches),",
         "# each scaled by the factor that maps the same counter's reading for a plain",
         "# elementwise copy (torch.neg, %d bytes read and %d written) onto its known size." % (COPY_BYTES, COPY_BYTES),
