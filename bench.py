@@ -359,6 +359,60 @@ def decode_set(torch, q4, lib, workload, warmup, steps, side_steps):
             "set_bytes": set_bytes, "per_matrix": per, "copies": copies}
 
 
+def graph_rate(torch, lib, fn, prod, launches, replays):
+    """Per-launch duration (s) of `launches` back-to-back launches of `fn`
+    (launch i on weight copy i) captured in one HIP graph, so host launch cost
+    is excluded; the graph's result is checked against an eager launch."""
+    sh = torch.cuda.current_stream().cuda_stream
+    launch(lib, fn, prod.args(launches - 1), sh)
+    torch.cuda.synchronize()
+    eager = prod.y.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(launches):
+            launch(lib, fn, prod.args(i), h)
+    torch.cuda.synchronize()
+    prod.y.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(prod.y, eager):
+        raise RuntimeError("%s graph differs from the eager launch" % fn)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (replays * launches) / 1e3
+
+
+def small_gemv_latency(torch, q4, lib):
+    """The latency-bound end: the single 1024 x 1024 GEMV and a one-row,
+    one-group GEMV (the cost of any launch through the library), both from a
+    graph of back-to-back launches."""
+    import q4_inputs as qi
+    out = {}
+    for key, mat in (("single_1024", qi.WORKLOADS["single"].cases[0][0]),
+                     ("launch_floor", qi.Matrix("floor", 1, 32, 0))):
+        x = torch.from_numpy(qi.activations(1, mat.k)).cuda()
+        p = Product(torch, q4, mat, 1, x, 64)
+        t = graph_rate(torch, lib, "q4_gemv", p, 64, 20)
+        out[key] = {"matrix": mat.name, "n": mat.n, "k": mat.k, "us": round(t * 1e6, 3),
+                    "GB_s": round(p.bytes / t / 1e9, 1),
+                    "hbm_frac": round(p.bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del p
+    torch.cuda.empty_cache()
+    return out
+
+
 def lm_head_rate(torch, q4, lib, mat, iters):
     """Back-to-back m = 1 LM-head GEMVs over rotated weight copies."""
     import q4_inputs as qi
@@ -645,6 +699,7 @@ def main() -> int:
     log("F16 GEMV LM head 0.8B")
     detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
     log("prefill GEMM M=512")
+    detail["small_gemv_latency"] = small_gemv_latency(torch, q4, lib)
     detail["gemm_m512"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
     detail["f16_gemm_m512"] = f16_gemv_rate(torch, q4, lib, qi.PREFILL_4B, 512, 100,
                                             fn="q4_gemm_f16", outliers=True)
