@@ -29,26 +29,8 @@ __device__ __forceinline__ uint32_t as_u32(half2_t h) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// Eight codes of one packed dword -> eight exact fp16 levels.
-// Dword bits: code of element e (0..7) sits at bits 4e..4e+3.
-// Output order (lo half, hi half) per register: (e0,e4) (e1,e5) (e2,e6) (e3,e7),
-// i.e. the fp16 at position v of the 8-vector is element kUnpackOrder[v].
-__device__ __forceinline__ half8_t unpack8(uint32_t d) {
-    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    half2_t h0 = as_half2((d & kNibblePairMask) | kMagic1024x2) + bias;
-    half2_t h1 = as_half2(((d >> 4) & kNibblePairMask) | kMagic1024x2) + bias;
-    half2_t h2 = as_half2(((d >> 8) & kNibblePairMask) | kMagic1024x2) + bias;
-    half2_t h3 = as_half2(((d >> 12) & kNibblePairMask) | kMagic1024x2) + bias;
-    half8_t r;
-    r[0] = h0[0]; r[1] = h0[1];
-    r[2] = h1[0]; r[3] = h1[1];
-    r[4] = h2[0]; r[5] = h2[1];
-    r[6] = h3[0]; r[7] = h3[1];
-    return r;
-}
-
 // Eight consecutive fp16 activations (as four dwords x0x1, x2x3, x4x5, x6x7)
-// reordered to match unpack8: (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+// reordered to match unpack8_fma: (x0,x4) (x1,x5) (x2,x6) (x3,x7).
 __device__ __forceinline__ u32x4_t permute_x8(u32x4_t d) {
     u32x4_t r;
     r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
@@ -82,7 +64,7 @@ __device__ __forceinline__ uint32_t to_vgpr(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, false);
 }
 
-// The same table lookup as unpack8, returned as four fp16 pairs
+// The same table lookup as unpack8_fma, returned as four fp16 pairs
 // (e0,e4) (e1,e5) (e2,e6) (e3,e7) for v_dot2_f32_f16.  mask and magic are
 // kNibblePairMask and kMagic1024x2 held in registers by the caller.
 __device__ __forceinline__ void unpack8_pairs(uint32_t d, uint32_t mask, uint32_t magic,
@@ -92,6 +74,35 @@ __device__ __forceinline__ void unpack8_pairs(uint32_t d, uint32_t mask, uint32_
     h[1] = as_half2(((d >> 4) & mask) | magic) + bias;
     h[2] = as_half2(((d >> 8) & mask) | magic) + bias;
     h[3] = as_half2(((d >> 12) & mask) | magic) + bias;
+}
+
+// Eight codes of one packed dword -> eight exact fp16 levels, for an MFMA
+// operand.  Dword bits: code of element e (0..7) sits at bits 4e..4e+3.
+// Output order (lo half, hi half) per register: (e0,e4) (e1,e5) (e2,e6)
+// (e3,e7), i.e. position v of the 8-vector holds element (v >> 1) + 4 (v & 1)
+// (activations are permuted to match with permute_x8).
+// Codes at bits 0..3 of a byte are spliced into 1024.0 and take -1032; codes
+// at bits 4..7 are spliced where they stand (1024 + 16 v) and one fp16 fma
+// with 1/16 and -72 gives v - 8 -- exact, since every intermediate is a small
+// integer or an exact multiple -- so the dword needs one shift, four
+// and-or splices and four packed fp16 operations.  mask, mask16 and magic are
+// kNibblePairMask, kNibblePairMask16 and kMagic1024x2 held in registers.
+__device__ __forceinline__ half8_t unpack8_fma(uint32_t d, uint32_t mask, uint32_t mask16,
+                                               uint32_t magic) {
+    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2_t bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t d8 = d >> 8;
+    const half2_t h0 = as_half2((d & mask) | magic) + bias;
+    const half2_t h1 = __builtin_elementwise_fma(as_half2((d & mask16) | magic), sixteenth, bias16);
+    const half2_t h2 = as_half2((d8 & mask) | magic) + bias;
+    const half2_t h3 = __builtin_elementwise_fma(as_half2((d8 & mask16) | magic), sixteenth, bias16);
+    half8_t r;
+    r[0] = h0[0]; r[1] = h0[1];
+    r[2] = h1[0]; r[3] = h1[1];
+    r[4] = h2[0]; r[5] = h2[1];
+    r[6] = h3[0]; r[7] = h3[1];
+    return r;
 }
 
 // The table lookup with one shift fewer, for v_dot2_f32_f16 with two sums.

@@ -27,7 +27,7 @@
 // a second MFMA chain on the same unpacked B.
 //
 // Activations are staged once per workgroup in LDS, permuted inside every
-// 8-element chunk to the order unpack8 produces codes in, so A and B agree
+// 8-element chunk to the order unpack8_fma produces codes in, so A and B agree
 // element by element.  Scales are read as 8 consecutive fp16 per lane (one
 // 16-byte load when the scale rows are 16-byte aligned).
 //
@@ -96,7 +96,8 @@ __device__ __forceinline__ Tile load_tile(const uint8_t* __restrict__ prow,
 // off-diagonal lanes read as their A operand.
 template <int TB>
 __device__ __forceinline__ void compute_tile(const Tile& t, const _Float16* xs,
-                                             int cg, int jl0, int lane,
+                                             int cg, int jl0, int lane, uint32_t mask,
+                                             uint32_t mask16, uint32_t magic,
                                              half8_t (&a)[TB][4], float (&acc)[TB]) {
     const int kb = lane >> 4;
     const bool diag = (lane & 3) == kb;          // A row (lane%16) = 4*tau + slot
@@ -112,7 +113,7 @@ __device__ __forceinline__ void compute_tile(const Tile& t, const _Float16* xs,
         const u32x4_t p = set ? t.p1 : t.p0;
         half8_t b[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) b[q] = unpack8(p[q]);
+        for (int q = 0; q < 4; ++q) b[q] = unpack8_fma(p[q], mask, mask16, magic);
         const int jl = jl0 + 4 * set + kb;       // local group of this lane's A slot
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
@@ -177,7 +178,8 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
                                           const uint8_t* __restrict__ packed,
                                           const uint16_t* __restrict__ scales,
                                           float* __restrict__ y, _Float16* xs, int M,
-                                          int64_t N, int K, int G, int64_t RB) {
+                                          int64_t N, int K, int G, int64_t RB,
+                                          const SpliceConsts& kc) {
     const int lane = threadIdx.x & 63;
     const int kb = lane >> 4;
     const int64_t W = (int64_t)gridDim.x * kGemvWaves;
@@ -215,6 +217,7 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
     stage_x<TB>(x, xs, M, K, G, 0, T * kTileGroups);
     __syncthreads();
 
+    const uint32_t magic = to_vgpr(kc.magic);
     half8_t a[TB][4];
     float acc[TB];
 #pragma unroll
@@ -236,7 +239,8 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
     for (; f0 + kPrefetch < F; f0 += kPrefetch) {
 #pragma unroll
         for (int p = 0; p < kPrefetch; ++p) {
-            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, a, acc);
+            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, kc.mask, kc.mask16,
+                             magic, a, acc);
             ring[p] = load_next();
             finish();
         }
@@ -244,7 +248,8 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int p = 0; p < kPrefetch; ++p) {
         if (f0 + p < F) {
-            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, a, acc);
+            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, kc.mask, kc.mask16,
+                             magic, a, acc);
             finish();
         }
     }
@@ -259,10 +264,11 @@ __device__ __forceinline__ void gemv_chunked(const uint16_t* __restrict__ x,
                                              const uint16_t* __restrict__ scales,
                                              float* __restrict__ y, _Float16* xs, int M,
                                              int64_t N, int K, int G, int chunk_groups,
-                                             int nchunks, int64_t RB) {
+                                             int nchunks, int64_t RB, const SpliceConsts& kc) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int kb = lane >> 4;
+    const uint32_t magic = to_vgpr(kc.magic);
     const int64_t per_round = (int64_t)gridDim.x * kGemvWaves;
     const int64_t iters = (RB + per_round - 1) / per_round;
     half8_t a[TB][4];
@@ -293,7 +299,8 @@ __device__ __forceinline__ void gemv_chunked(const uint16_t* __restrict__ x,
                     for (int p = 0; p < kPrefetch; ++p) {
                         const int tt = t0 + p;
                         if (tt < ntiles) {
-                            compute_tile<TB>(ring[p], xs, cg, tt * kTileGroups, lane, a, acc);
+                            compute_tile<TB>(ring[p], xs, cg, tt * kTileGroups, lane, kc.mask,
+                                             kc.mask16, magic, a, acc);
                             if (tt + kPrefetch < ntiles)
                                 ring[p] = load_tile<kScale16>(
                                     prow, srow, jc0 + (tt + kPrefetch) * kTileGroups, kb, G);
@@ -310,14 +317,14 @@ template <int TB, bool kScale16>
 __global__ __launch_bounds__(kGemvThreads, 2) void gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, float* __restrict__ y, int M, int64_t N, int K,
-    int G, int chunk_groups, int nchunks, int64_t RB) {
+    int G, int chunk_groups, int nchunks, int64_t RB, SpliceConsts kc) {
     extern __shared__ __align__(16) unsigned char smem[];
     _Float16* xs = reinterpret_cast<_Float16*>(smem);
     if (nchunks == 1)
-        gemv_flat<TB, kScale16>(x, packed, scales, y, xs, M, N, K, G, RB);
+        gemv_flat<TB, kScale16>(x, packed, scales, y, xs, M, N, K, G, RB, kc);
     else
         gemv_chunked<TB, kScale16>(x, packed, scales, y, xs, M, N, K, G, chunk_groups, nchunks,
-                                   RB);
+                                   RB, kc);
 }
 
 template <int TB, bool kScale16>
@@ -350,7 +357,7 @@ hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
     const int blocks = (int)(blocks64 > 0 ? blocks64 : 1);
     const size_t lds = (size_t)per_group_bytes * chunk + fixed_bytes;
     hipLaunchKernelGGL((gemv_kernel<TB, kScale16>), dim3(blocks), dim3(kGemvThreads), lds,
-                       stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB);
+                       stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB, kSpliceConsts);
     return hipGetLastError();
 }
 
