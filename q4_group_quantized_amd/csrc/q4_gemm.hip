@@ -29,8 +29,9 @@
 // so the loop body issues no register-destination global loads and the only
 // waits on global memory are the explicit per-stage vmcnt waits below.
 // Rows past M, columns past N and groups past G are clamped to real
-// addresses: their results are never stored, and out-of-range groups are
-// never computed.
+// addresses: their results are never stored.  Groups past the end of a
+// wave's K slice read zero activations and a zero scale from a block of LDS
+// kept for that, so they add exactly 0 and the loop has no per-group branch.
 #include "q4.h"
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
@@ -61,6 +62,9 @@ struct Gemm {
     static constexpr int groups_of(int wn) { return (KG * H - wn + WN - 1) / WN; }
     static constexpr int loads_per_stage(int wn) { return kABlocksPerWave + 2 * groups_of(wn); }
     static constexpr int kLdsBytes = WK * S * kStageBytes;
+    // zeros that the operand reads of out-of-range groups are pointed at
+    static constexpr int kZeroBytes = MB * kBlockBytes;
+    static constexpr int kLdsTotal = kLdsBytes + kZeroBytes;
     static constexpr int kRedBytes = (WK - 1) * WN * MB * 8 * 64 * 4;
     static constexpr int kThreads = 64 * WN * WK;
     static_assert(WN * WK == 4 || WN * WK == 8, "one or two waves per SIMD");
@@ -68,7 +72,8 @@ struct Gemm {
     static_assert((KG * MB) % WN == 0, "activation blocks split evenly");
     static_assert(S >= 2, "at least double buffering");
     static_assert(kRedBytes <= kLdsBytes, "reduction fits in the staging space");
-    static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+    static_assert(kLdsTotal <= 160 * 1024, "LDS of one CU");
+    static_assert(4 * BN <= kZeroBytes, "zero scale slots of every column");
 };
 
 // The matrices of one launch: up to kGemmMaxSegments weight matrices over the
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const int64_t tile = (int64_t)blockIdx.x - tile0;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar branches
     const int wn = wave % WN;
     const int kp = wave / WN;
     const int64_t nt0 = (tile % tiles_n) * C::BN;     // tile's first column
@@ -125,6 +130,14 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const int nstages = (Gp + KG - 1) / KG;               // same for every wave
 
     unsigned char* kbase = smem + (size_t)kp * S * C::kStageBytes;
+    // A group past the slice's end (the last stage of a slice whose group
+    // count is not a multiple of KG) reads its activations and scale from
+    // this zero block: its MFMA then gives exactly 0 (levels are finite) and
+    // its scale FMA adds 0 * 0, so every group is computed without a branch.
+    const unsigned char* zero = smem + C::kLdsBytes;
+    for (int i = threadIdx.x; i < C::kZeroBytes / 16; i += C::kThreads)
+        reinterpret_cast<u32x4_t*>(smem + C::kLdsBytes)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): zeros stored before the first barrier
     // Workgroups start their walk over K at different stages so that the CUs
     // sharing an L2 do not all request the same activation columns at once.
     // The order of the fp32 sums changes with it, identically on every run.
@@ -194,18 +207,18 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
         uint32_t code[2];
         _Float16 sc[2];
     };
-    auto read_ops = [&](Ops& o, const unsigned char* sb, int gl) {
+    auto read_ops = [&](Ops& o, const unsigned char* sb, int gl, bool valid) {
+        const unsigned char* ab = valid ? sb + gl * MB * kBlockBytes : zero;
+        const unsigned char* scb = valid ? sb + C::kScaleOff + gl * C::H * 256 : zero;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-            o.a[mb] = *reinterpret_cast<const half8_t*>(sb + (gl * MB + mb) * kBlockBytes +
-                                                        64 * col + 16 * kq);
+            o.a[mb] = *reinterpret_cast<const half8_t*>(ab + mb * kBlockBytes + 64 * col + 16 * kq);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int c = 32 * wn + 16 * nb + col;
             o.code[nb] = *reinterpret_cast<const uint32_t*>(
                 sb + C::kCodeOff + gl * C::H * kBlockBytes + 16 * c + 4 * kq);
-            o.sc[nb] = *reinterpret_cast<const _Float16*>(sb + C::kScaleOff + gl * C::H * 256 +
-                                                          4 * c);
+            o.sc[nb] = *reinterpret_cast<const _Float16*>(scb + 4 * c);
         }
     };
     auto compute = [&](const Ops& o) {
@@ -253,11 +266,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
                 const unsigned char* sb = kbase + u * C::kStageBytes;
                 const int g0 = gbeg + stage_group(st);
                 Ops ops[2];
-                read_ops(ops[0], sb, 0);
+                read_ops(ops[0], sb, 0, g0 < gend);
 #pragma unroll
                 for (int gl = 0; gl < KG; ++gl) {
-                    if (gl + 1 < KG) read_ops(ops[(gl + 1) & 1], sb, gl + 1);
-                    if (g0 + gl < gend) compute(ops[gl & 1]);
+                    if (gl + 1 < KG) read_ops(ops[(gl + 1) & 1], sb, gl + 1, g0 + gl + 1 < gend);
+                    compute(ops[gl & 1]);
                 }
             }
         }
@@ -320,12 +333,12 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
             reinterpret_cast<const void*>(&gemm_kernel<BM, WN, WK, KG, S>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsTotal);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
-                       dim3(C::kThreads), C::kLdsBytes, stream, x, seg, (int)m, (int)k,
+                       dim3(C::kThreads), C::kLdsTotal, stream, x, seg, (int)m, (int)k,
                        (int)(k / 32), kSpliceConsts);
     return hipGetLastError();
 }

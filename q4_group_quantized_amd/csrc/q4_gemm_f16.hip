@@ -20,7 +20,9 @@
 // the weight rows alike; each lane reads an operand with one ds_read_b128.
 // The WK partial tiles are added in LDS in a fixed order (deterministic).
 // Rows past M or N and K steps past K/32 are clamped to real addresses: their
-// results are never stored and out-of-range steps are never computed.
+// results are never stored.  K steps past the end of a wave's K slice read
+// both operands from a block of zeros in LDS, so they add exactly 0 and the
+// loop has no per-step branch.
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
 
@@ -47,13 +49,16 @@ struct GemmF16 {
     static constexpr int kWBlocksPerWave = KG * NB / WN;
     static constexpr int kLoadsPerStage = kABlocksPerWave + kWBlocksPerWave;
     static constexpr int kLdsBytes = WK * S * kStageBytes;
+    // zeros that the operand reads of out-of-range K steps are pointed at
+    static constexpr int kZeroBytes = (MB > NB ? MB : NB) * kF16Block;
+    static constexpr int kLdsTotal = kLdsBytes + kZeroBytes;
     static constexpr int kRedBytes = (WK - 1) * WN * MB * 8 * 64 * 4;
     static constexpr int kThreads = 64 * WN * WK;
     static_assert(WN * WK == 4 || WN * WK == 8, "one or two waves per SIMD");
     static_assert((KG * MB) % WN == 0, "activation blocks split evenly");
     static_assert(S >= 2, "at least double buffering");
     static_assert(kRedBytes <= kLdsBytes, "reduction fits in the staging space");
-    static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+    static_assert(kLdsTotal <= 160 * 1024, "LDS of one CU");
 };
 
 // At least two waves per SIMD: caps a wave at 256 registers, which keeps the
@@ -68,7 +73,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_f16_kernel(
 
     const int64_t tile = blockIdx.x;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar branches
     const int wn = wave % WN;
     const int kp = wave / WN;
     const int64_t nt0 = (tile % tiles_n) * C::BN;     // tile's first column
@@ -80,6 +85,12 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_f16_kernel(
     const int nstages = (Gp + KG - 1) / KG;           // same for every wave
 
     unsigned char* kbase = smem + (size_t)kp * S * C::kStageBytes;
+    // zero operands for K steps past the slice's end (both operands: a zero
+    // weight times an infinite activation, or the reverse, would be NaN)
+    const unsigned char* zero = smem + C::kLdsBytes;
+    for (int i = threadIdx.x; i < C::kZeroBytes / 16; i += C::kThreads)
+        reinterpret_cast<u32x4_t*>(smem + C::kLdsBytes)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): zeros stored before the first barrier
     // Workgroups start their walk over K at different stages so that the CUs
     // sharing an L2 do not all request the same columns at once; the order of
     // the fp32 sums depends only on the tile index, identically on every run.
@@ -133,15 +144,16 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_f16_kernel(
         half8_t a[MB];
         half8_t b[2];
     };
-    auto read_ops = [&](Ops& o, const unsigned char* sb, int gl) {
+    auto read_ops = [&](Ops& o, const unsigned char* sb, int gl, bool valid) {
+        const unsigned char* ab = valid ? sb + gl * MB * kF16Block : zero;
+        const unsigned char* bb = valid ? sb + C::kWOff + gl * C::NB * kF16Block : zero;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-            o.a[mb] = *reinterpret_cast<const half8_t*>(sb + (gl * MB + mb) * kF16Block +
-                                                        64 * col + 16 * kq);
+            o.a[mb] = *reinterpret_cast<const half8_t*>(ab + mb * kF16Block + 64 * col + 16 * kq);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-            o.b[nb] = *reinterpret_cast<const half8_t*>(
-                sb + C::kWOff + (gl * C::NB + 2 * wn + nb) * kF16Block + 64 * col + 16 * kq);
+            o.b[nb] = *reinterpret_cast<const half8_t*>(bb + (2 * wn + nb) * kF16Block +
+                                                        64 * col + 16 * kq);
     };
     auto compute = [&](const Ops& o) {
 #pragma unroll
@@ -166,11 +178,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_f16_kernel(
                 const unsigned char* sb = kbase + u * C::kStageBytes;
                 const int g0 = gbeg + stage_step(st);
                 Ops ops[2];
-                read_ops(ops[0], sb, 0);
+                read_ops(ops[0], sb, 0, g0 < gend);
 #pragma unroll
                 for (int gl = 0; gl < KG; ++gl) {
-                    if (gl + 1 < KG) read_ops(ops[(gl + 1) & 1], sb, gl + 1);
-                    if (g0 + gl < gend) compute(ops[gl & 1]);
+                    if (gl + 1 < KG) read_ops(ops[(gl + 1) & 1], sb, gl + 1, g0 + gl + 1 < gend);
+                    compute(ops[gl & 1]);
                 }
             }
         }
@@ -222,12 +234,12 @@ hipError_t launch_gemm_f16_t(const uint16_t* x, const uint16_t* w, float* y, int
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
             reinterpret_cast<const void*>(&gemm_f16_kernel<BM, WN, WK, KG, S>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsTotal);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     hipLaunchKernelGGL((gemm_f16_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
-                       dim3(C::kThreads), C::kLdsBytes, stream, x, w, y, (int)m, n, (int)k,
+                       dim3(C::kThreads), C::kLdsTotal, stream, x, w, y, (int)m, n, (int)k,
                        (int)(k / 32), tiles_n);
     return hipGetLastError();
 }
