@@ -60,6 +60,7 @@ __device__ __forceinline__ uint64_t merge_sorted(uint64_t a, uint64_t b, int lan
 }
 
 constexpr int kCandCap = 2048;
+constexpr int kCandBatch = 8;         // keys per thread loaded before testing
 
 // One workgroup per token over its lists partials[t * lists .. + lists), each
 // sorted descending.
@@ -104,13 +105,24 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
     }
     const uint64_t thr = wave_lists[0][topk - 1];
 
-    // 2. candidates
+    // 2. candidates: each thread loads kCandBatch keys before testing any of
+    // them, so their global loads are in flight together (one load per
+    // iteration waited for every key in turn: ~16 round trips at m = 1)
     const int64_t total = lists * kTopkList;
-    for (int64_t i = threadIdx.x; i < total; i += 64 * kMergeWaves) {
-        const uint64_t key = src[i];
-        if (key >= thr && key != 0) {
-            const uint32_t pos = atomicAdd(&ncand, 1u);
-            if (pos < kCandCap) cand[pos] = key;
+    constexpr int64_t kStride = 64 * kMergeWaves;
+    for (int64_t i0 = threadIdx.x; i0 < total; i0 += kStride * kCandBatch) {
+        uint64_t keys[kCandBatch];
+#pragma unroll
+        for (int b = 0; b < kCandBatch; ++b) {
+            const int64_t i = i0 + b * kStride;
+            keys[b] = i < total ? src[i] : 0;
+        }
+#pragma unroll
+        for (int b = 0; b < kCandBatch; ++b) {
+            if (keys[b] >= thr && keys[b] != 0) {
+                const uint32_t pos = atomicAdd(&ncand, 1u);
+                if (pos < kCandCap) cand[pos] = keys[b];
+            }
         }
     }
     __syncthreads();
