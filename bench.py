@@ -20,7 +20,9 @@ value    = algorithmic bytes of one step / step time (GB/s); algorithmic bytes
 roofline = the dominant kernel (the LM-head GEMV): its algorithmic bytes per
            launch / its average launch duration (HIP events on the launching
            stream around a batch of back-to-back launches over the rotated
-           copies), against the 8 TB/s HBM3E peak
+           copies, after ~20 ms of untimed launches of the same kernel: every
+           timed batch here starts past the clock ramp of sustained traffic),
+           against the 8 TB/s HBM3E peak
 detail   = the other halves of the hot path measured in the same run: the 4B
            LM head (k = 2560), the 0.8B LM head with its top-20 epilogue
            (q4_gemv_topk, against q4_gemv + torch.topk), the 0.8B LM head in
@@ -230,12 +232,36 @@ def launch(lib, fn, args, stream):
         raise RuntimeError("%s failed with status %d" % (fn, st))
 
 
+# Untimed work of the same kind before every timed batch.  After lighter work
+# the first ~10 ms of sustained HBM traffic run up to ~15% slower than the
+# steady state (measured on the 0.8B LM head: 28 us per launch for the first
+# ~350 back-to-back launches, then 24.4-24.7 us, with 2 or 8 rotated copies
+# alike), so each batch is timed only after that ramp.
+SETTLE_S = 0.02
+
+
+def settle(torch, fn):
+    """Runs fn(i) untimed for about SETTLE_S seconds of GPU time."""
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(10):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    per = max(a.elapsed_time(b) / 10 / 1e3, 1e-6)
+    for i in range(min(20000, int(SETTLE_S / per))):
+        fn(i)
+    torch.cuda.synchronize()
+
+
 def time_launches(torch, lib, fn, prod, iters, stream_handle):
     """Average duration (s) of `iters` back-to-back launches rotating through
-    the weight copies: HIP events on the launching stream around the batch."""
-    for i in range(3):
-        launch(lib, fn, prod.args(i), stream_handle)
-    torch.cuda.synchronize()
+    the weight copies: HIP events on the launching stream around the batch
+    (after SETTLE_S of untimed launches)."""
+    settle(torch, lambda i: launch(lib, fn, prod.args(i), stream_handle))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(iters):
@@ -443,9 +469,7 @@ def f16_gemv_rate(torch, q4, lib, mat, m, iters, fn="q4_gemv_f16", outliers=Fals
         st = call(x.data_ptr(), ws[i % copies].data_ptr(), y.data_ptr(), m, mat.n, mat.k, sh)
         if st != 0:
             raise RuntimeError("%s failed with status %d" % (fn, st))
-    for i in range(3):
-        go(i)
-    torch.cuda.synchronize()
+    settle(torch, go)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(iters):
@@ -491,9 +515,7 @@ def topk_rate(torch, q4, lib, mat, m, topk, iters):
         torch.topk(p.y, topk, dim=1)
 
     def timed(fn):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
+        settle(torch, fn)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(iters):
@@ -531,9 +553,7 @@ def gemm_multi_rate(torch, q4, lib, mats, m, iters):
             launch(lib, "q4_gemm", p.args(0), sh)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        settle(torch, lambda i: fn())
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(iters):
@@ -573,8 +593,7 @@ def quantize_rate(torch, q4, mat, iters):
     w = torch.from_numpy(qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)).cuda()
     packed = torch.empty((mat.n, mat.k // 2), dtype=torch.uint8, device=w.device)
     scales = torch.empty((mat.n, mat.k // 32), dtype=torch.float16, device=w.device)
-    q4.q4_quantize(w, out=(packed, scales))
-    torch.cuda.synchronize()
+    settle(torch, lambda i: q4.q4_quantize(w, out=(packed, scales)))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(iters):
@@ -631,7 +650,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--all", action="store_true", help="also time the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rocprof-summary", metavar="TRACE_CSV_OR_DB")
