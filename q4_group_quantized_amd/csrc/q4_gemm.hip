@@ -329,14 +329,10 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
         tiles += seg.tiles_n[i] * ((m + BM - 1) / BM);
     }
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&gemm_kernel<BM, WN, WK, KG, S>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsTotal);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_done{0};           // devices already set up
+    hipError_t e = allow_dynamic_lds(
+        reinterpret_cast<const void*>(&gemm_kernel<BM, WN, WK, KG, S>), C::kLdsTotal, lds_done);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
                        dim3(C::kThreads), C::kLdsTotal, stream, x, seg, (int)m, (int)k,
                        (int)(k / 32), kSpliceConsts);

@@ -230,14 +230,10 @@ hipError_t launch_gemm_f16_t(const uint16_t* x, const uint16_t* w, float* y, int
     const int64_t tiles_n = (n + C::BN - 1) / C::BN;
     const int64_t tiles = tiles_n * ((m + BM - 1) / BM);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&gemm_f16_kernel<BM, WN, WK, KG, S>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsTotal);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_done{0};           // devices already set up
+    hipError_t e = allow_dynamic_lds(
+        reinterpret_cast<const void*>(&gemm_f16_kernel<BM, WN, WK, KG, S>), C::kLdsTotal, lds_done);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_f16_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
                        dim3(C::kThreads), C::kLdsTotal, stream, x, w, y, (int)m, n, (int)k,
                        (int)(k / 32), tiles_n);

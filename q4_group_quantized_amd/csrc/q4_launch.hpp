@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace q4 {
 
 struct DeviceInfo {
@@ -17,6 +19,11 @@ const DeviceInfo& device_info(int device);
 
 // True when `device` (0 <= device < 64) is a gfx950 the kernels were built for.
 bool device_usable(int device);
+
+// Allows `kernel` `bytes` of dynamic LDS on the current device.  The setting
+// is made once per device (bit d of `done` records device d); safe to call
+// from several threads.
+hipError_t allow_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done);
 
 hipError_t launch_quantize(const float* w, uint8_t* packed, uint16_t* scales,
                            int64_t n, int64_t k, hipStream_t stream);
