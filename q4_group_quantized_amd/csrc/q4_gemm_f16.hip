@@ -91,10 +91,12 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_f16_kernel(
     for (int i = threadIdx.x; i < C::kZeroBytes / 16; i += C::kThreads)
         reinterpret_cast<u32x4_t*>(smem + C::kLdsBytes)[i] = u32x4_t{0u, 0u, 0u, 0u};
     __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): zeros stored before the first barrier
-    // Workgroups start their walk over K at different stages so that the CUs
-    // sharing an L2 do not all request the same columns at once; the order of
-    // the fp32 sums depends only on the tile index, identically on every run.
-    const int rot = (int)(tile % nstages);
+    // Workgroups start their walk over K at a stage set by their column tile:
+    // tiles of different columns spread their requests for the same activation
+    // rows over K, while the row tiles of one column walk its weights in step
+    // and share them in L2 (fp16 weights far exceed it).  The order of the
+    // fp32 sums depends only on the tile index, identically on every run.
+    const int rot = (int)((tile % tiles_n) % nstages);
     auto stage_step = [&](int st) {               // first K step (in the slice) of stage st
         const int r = st + rot;
         return (r < nstages ? r : r - nstages) * KG;
