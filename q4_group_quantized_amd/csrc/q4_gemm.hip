@@ -140,9 +140,9 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): zeros stored before the first barrier
     // Workgroups start their walk over K at a stage set by their column tile:
     // tiles of different columns spread their requests for the same activation
-    // rows over K, while the row tiles of one column (on one XCD: the tile
-    // count per row is a multiple of 8 for every n used here, else merely
-    // spread) walk its weights in step and share them in L2.  The order of
+    // rows over K, while the row tiles of one column (on one XCD when the
+    // number of column tiles is a multiple of 8) walk its weights in step and
+    // share them in L2.  The order of
     // the fp32 sums depends only on the tile index, identically on every run.
     const int rot = (int)((tile % tiles_n) % nstages);
     auto stage_group = [&](int st) {               // first group (in the slice) of stage st
