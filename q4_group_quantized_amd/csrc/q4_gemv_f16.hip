@@ -13,11 +13,14 @@
 // block's K in steps of four 32-element groups (16 rows x 256 bytes: whole
 // cache lines), with PF steps of loads in flight.  Lane (r, kq) = (lane % 16,
 // lane / 16) loads weight row r's eight elements at K offset 8 kq of every
-// group (the MFMA B layout) and activation row r's matching eight elements
-// (the A layout; rows r >= m read nothing and stay zero).  One MFMA per group
+// group (the MFMA B layout) and reads activation row r's matching eight
+// elements (the A layout; rows r >= m are zero).  One MFMA per group
 // accumulates D[token][row] over the whole K; the block's results are stored
 // when its last step is done.  No dequantization and no per-group scaling:
-// the kernel is a pure stream of 2 bytes per weight.
+// the kernel is a pure stream of 2 bytes per weight.  The activations are
+// staged once per workgroup in LDS (gemv_f16_lds_kernel) whenever they fit;
+// gemv_f16_kernel, which reads them from global memory at every step, serves
+// larger k.
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
 
@@ -115,6 +118,119 @@ __global__ __launch_bounds__(kF16Threads, 1) void gemv_f16_kernel(
 #pragma unroll
     for (int p = 0; p < PF; ++p)
         if (f0 + p < F) compute(ring[p]);
+}
+
+// The same product with the activations staged in LDS once per workgroup:
+// 9 rows of Kp halves (tokens 0..7, zero past m, then a zero row that A rows
+// 8..15 read), Kp = k padded with zeros to whole steps.  Against re-reading
+// the activations from L2 at every step this halves the kernel's load
+// instructions (measured on the 248,320-row heads: m = 8, k = 2560 326.8 ->
+// 272.5 us; k = 1024 117.5 -> 101 us; bit-identical).  The load cursor
+// advances with selects, so the loop has no per-step branch.
+template <int PF>
+__global__ __launch_bounds__(kF16Threads, 2) void gemv_f16_lds_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ y,
+    int M, int64_t N, int K, int G, int Kp, int64_t base, int64_t extra) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    _Float16* xs = reinterpret_cast<_Float16*>(smem);
+    const int cpr = Kp / 8;                                   // 16-byte chunks per LDS row
+    for (int u = threadIdx.x; u < 9 * cpr; u += kF16Threads) {
+        const int row = u / cpr, c = u % cpr;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row < M && 8 * c < K)
+            v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)row * K + 8 * c);
+        *reinterpret_cast<u32x4_t*>(xs + (int64_t)row * Kp + 8 * c) = v;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int64_t wv = (int64_t)blockIdx.x * kF16Waves +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t rb0 = wv * base + (wv < extra ? wv : extra);
+    const int64_t cnt = base + (wv < extra ? 1 : 0);
+    if (cnt <= 0) return;
+    const int T = Kp / (32 * kStepGroups);                    // steps per row block
+    const int64_t F = cnt * T;
+    const _Float16* xa = xs + (int64_t)(r < M ? r : 8) * Kp + 8 * kq;
+    // load cursor; steps past the wave's range re-read row n - 1
+    const int64_t rb_end = rb0 + cnt;
+    int64_t lrb = rb0;
+    int lt = 0;
+    auto load_next = [&]() -> F16Step {
+        F16Step s;
+        const int64_t n = lrb * 16 + r;
+        const int64_t nc = (lrb < rb_end && n < N) ? n : N - 1;
+        const uint16_t* wrow = w + nc * (int64_t)K + 8 * kq;
+#pragma unroll
+        for (int q = 0; q < kStepGroups; ++q) {
+            const int g = lt * kStepGroups + q;
+            const int gc = g < G ? g : G - 1;
+            s.w[q] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(wrow + 32 * gc));
+        }
+        const int nt = lt + 1;
+        const bool wrap = nt == T;
+        lt = wrap ? 0 : nt;
+        lrb += wrap ? 1 : 0;
+        return s;
+    };
+    F16Step ring[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) ring[p] = load_next();
+    float4_t d = {0.f, 0.f, 0.f, 0.f};
+    int64_t crb = rb0;
+    int ct = 0;
+    auto compute = [&](const F16Step& s) {
+#pragma unroll
+        for (int q = 0; q < kStepGroups; ++q) {
+            const half8_t a =
+                *reinterpret_cast<const half8_t*>(xa + 32 * (ct * kStepGroups + q));
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, s.w[q], d, 0, 0, 0);
+        }
+        if (++ct == T) {
+            // D[4 kq + v][r]: token 4 kq + v, weight row 16 crb + r
+            const int64_t n = crb * 16 + r;
+            if (n < N) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = 4 * kq + v;
+                    if (t < M) y[(int64_t)t * N + n] = d[v];
+                }
+            }
+            d = float4_t{0.f, 0.f, 0.f, 0.f};
+            ct = 0;
+            ++crb;
+        }
+    };
+    int64_t f0 = 0;
+    for (; f0 + PF < F; f0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            compute(ring[p]);
+            ring[p] = load_next();
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (f0 + p < F) compute(ring[p]);
+}
+
+template <int PF>
+hipError_t launch_f16_lds_t(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
+                            int64_t n, int64_t k, int Kp, int wps, int cu, hipStream_t stream) {
+    const size_t lds = (size_t)9 * Kp * 2;
+    static std::atomic<uint64_t> lds_done{0};           // devices already set up
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_f16_lds_kernel<PF>),
+                                     (int)lds, lds_done);
+    if (e != hipSuccess) return e;
+    const int64_t RB = (n + 15) / 16;
+    const int64_t max_waves = (int64_t)cu * kF16Waves * wps;
+    const int64_t per = (RB + max_waves - 1) / max_waves;
+    const int64_t waves = (RB + per - 1) / per;
+    const int blocks = (int)((waves + kF16Waves - 1) / kF16Waves);
+    const int64_t W = (int64_t)blocks * kF16Waves;
+    hipLaunchKernelGGL((gemv_f16_lds_kernel<PF>), dim3(blocks), dim3(kF16Threads), lds, stream,
+                       x, w, y, (int)m, n, (int)k, (int)(k / 32), Kp, RB / W, RB % W);
+    return hipGetLastError();
 }
 
 // m = 1: a streaming kernel without the matrix core.  LPR lanes share a row
@@ -251,17 +367,26 @@ hipError_t launch_f16_m1(const uint16_t* x, const uint16_t* w, float* y, int64_t
 }  // namespace
 
 // m = 1: the streaming kernel where k fits it; otherwise (and for m = 2..8)
-// the MFMA kernel, one wave per SIMD, each with a contiguous, balanced range
-// of row blocks.
+// the MFMA kernel, with each wave owning a contiguous, balanced range of row
+// blocks: the LDS-staged form while 9 rows of padded k fit in 160 KB of LDS
+// (k <= 9088), from a sweep of steps in flight x waves per SIMD on the
+// 248,320-row heads: 4 steps x 2 waves up to k = 1536, 8 steps x 1 wave above.
 hipError_t launch_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
                            int64_t n, int64_t k, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    const int cu = device_info(dev).cu_count;
     if (m == 1) {
         bool done = false;
-        e = launch_f16_m1(x, w, y, n, k, device_info(dev).cu_count, stream, done);
+        e = launch_f16_m1(x, w, y, n, k, cu, stream, done);
         if (done) return e;
+    }
+    const int64_t steps = (k / 32 + kStepGroups - 1) / kStepGroups;
+    const int64_t Kp = steps * 32 * kStepGroups;
+    if (9 * Kp * 2 <= 160 * 1024) {
+        if (k <= 1536) return launch_f16_lds_t<4>(x, w, y, m, n, k, (int)Kp, 2, cu, stream);
+        return launch_f16_lds_t<8>(x, w, y, m, n, k, (int)Kp, 1, cu, stream);
     }
     const int64_t RB = (n + 15) / 16;
     const int64_t max_waves = (int64_t)device_info(dev).cu_count * kF16Waves;
