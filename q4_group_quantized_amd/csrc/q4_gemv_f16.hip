@@ -17,10 +17,10 @@
 // elements (the A layout; rows r >= m are zero).  One MFMA per group
 // accumulates D[token][row] over the whole K; the block's results are stored
 // when its last step is done.  No dequantization and no per-group scaling:
-// the kernel is a pure stream of 2 bytes per weight.  The activations are
-// staged once per workgroup in LDS (gemv_f16_lds_kernel) whenever they fit;
-// gemv_f16_kernel, which reads them from global memory at every step, serves
-// larger k.
+// the kernel is a pure stream of 2 bytes per weight.  gemv_f16_lds_kernel
+// below (activations staged in LDS, weights read in whole row segments) runs
+// wherever its LDS fits; this form, which reads the activations from global
+// memory at every step, serves larger k.
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
 
@@ -120,13 +120,27 @@ __global__ __launch_bounds__(kF16Threads, 1) void gemv_f16_kernel(
         if (f0 + p < F) compute(ring[p]);
 }
 
-// The same product with the activations staged in LDS once per workgroup:
-// 9 rows of Kp halves (tokens 0..7, zero past m, then a zero row that A rows
-// 8..15 read), Kp = k padded with zeros to whole steps.  Against re-reading
-// the activations from L2 at every step this halves the kernel's load
-// instructions (measured on the 248,320-row heads: m = 8, k = 2560 326.8 ->
-// 272.5 us; k = 1024 117.5 -> 101 us; bit-identical).  The load cursor
-// advances with selects, so the loop has no per-step branch.
+// The same product with the activations staged in LDS once per workgroup and
+// the weights read in whole 256-byte row segments.  In the MFMA B layout a
+// wave load covers 16 rows x 64 bytes, which streams at ~5.3 TB/s; here lane
+// (lr, lj) = (lane / 16, lane % 16) loads the 16-byte chunk lj of row 4 i + lr
+// (i < 4), so each wave load covers 4 rows x 256 contiguous bytes, and every
+// step's 16 x 256-byte tile makes a round trip through a wave-private LDS
+// tile: chunk j of row n is stored at 256 n + 16 ((j + n) mod 16), a rotation
+// that keeps both the row-wise writes and the column-wise B-operand reads
+// (lane (r, kq) reads chunk 4 q + kq of row r for the step's MFMA q) free of
+// bank conflicts.  Two tiles per wave alternate between steps.  The k order
+// inside every MFMA is the one gemv_f16_kernel uses, so the results are the
+// same bits.  LDS: 9 rows of Kp halves (tokens 0..7, zero past m, and a zero
+// row that A rows 8..15 read; Kp = k padded with zeros to whole steps) plus
+// 8 KB per wave.  Measured on the 248,320-row heads, m = 8: k = 2560
+// 326.8 -> 204 us (78% of HBM), k = 1024 117.5 -> 88 us.
+constexpr int kTileBytes = 4096;                // 16 rows x 256 bytes
+
+struct F16Tile {
+    u32x4_t v[4];                               // row 4 i + lane / 16, chunk lane % 16
+};
+
 template <int PF>
 __global__ __launch_bounds__(kF16Threads, 2) void gemv_f16_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ y,
@@ -143,29 +157,32 @@ __global__ __launch_bounds__(kF16Threads, 2) void gemv_f16_lds_kernel(
     }
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int r = lane & 15, kq = lane >> 4;
-    const int64_t wv = (int64_t)blockIdx.x * kF16Waves +
-                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    unsigned char* tiles = smem + (size_t)9 * Kp * 2 + (size_t)wave * 2 * kTileBytes;
+    const int r = lane & 15, kq = lane >> 4;                  // MFMA operand layout
+    const int lr = lane >> 4, lj = lane & 15;                 // load layout
+    const int64_t wv = (int64_t)blockIdx.x * kF16Waves + wave;
     const int64_t rb0 = wv * base + (wv < extra ? wv : extra);
     const int64_t cnt = base + (wv < extra ? 1 : 0);
     if (cnt <= 0) return;
     const int T = Kp / (32 * kStepGroups);                    // steps per row block
     const int64_t F = cnt * T;
     const _Float16* xa = xs + (int64_t)(r < M ? r : 8) * Kp + 8 * kq;
-    // load cursor; steps past the wave's range re-read row n - 1
+    // load cursor; steps past the wave's range re-read row n - 1, groups past
+    // G re-read group G - 1 (their activations are zero)
     const int64_t rb_end = rb0 + cnt;
     int64_t lrb = rb0;
     int lt = 0;
-    auto load_next = [&]() -> F16Step {
-        F16Step s;
-        const int64_t n = lrb * 16 + r;
-        const int64_t nc = (lrb < rb_end && n < N) ? n : N - 1;
-        const uint16_t* wrow = w + nc * (int64_t)K + 8 * kq;
+    auto load_next = [&]() -> F16Tile {
+        F16Tile s;
+        const int g = lt * kStepGroups + (lj >> 2);
+        const int gc = g < G ? g : G - 1;
 #pragma unroll
-        for (int q = 0; q < kStepGroups; ++q) {
-            const int g = lt * kStepGroups + q;
-            const int gc = g < G ? g : G - 1;
-            s.w[q] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(wrow + 32 * gc));
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = lrb * 16 + 4 * i + lr;
+            const int64_t nc = (lrb < rb_end && n < N) ? n : N - 1;
+            s.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                w + nc * (int64_t)K + 32 * gc + 8 * (lj & 3)));
         }
         const int nt = lt + 1;
         const bool wrap = nt == T;
@@ -173,18 +190,29 @@ __global__ __launch_bounds__(kF16Threads, 2) void gemv_f16_lds_kernel(
         lrb += wrap ? 1 : 0;
         return s;
     };
-    F16Step ring[PF];
+    F16Tile ring[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) ring[p] = load_next();
     float4_t d = {0.f, 0.f, 0.f, 0.f};
     int64_t crb = rb0;
     int ct = 0;
-    auto compute = [&](const F16Step& s) {
+    int tsel = 0;
+    auto compute = [&](const F16Tile& s) {
+        unsigned char* tile = tiles + tsel * kTileBytes;
+        tsel ^= 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = 4 * i + lr;
+            *reinterpret_cast<u32x4_t*>(tile + 256 * n + 16 * ((lj + n) & 15)) = s.v[i];
+        }
 #pragma unroll
         for (int q = 0; q < kStepGroups; ++q) {
+            const int c = 4 * q + kq;                         // chunk of row r
+            const half8_t b =
+                *reinterpret_cast<const half8_t*>(tile + 256 * r + 16 * ((c + r) & 15));
             const half8_t a =
                 *reinterpret_cast<const half8_t*>(xa + 32 * (ct * kStepGroups + q));
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, s.w[q], d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d, 0, 0, 0);
         }
         if (++ct == T) {
             // D[4 kq + v][r]: token 4 kq + v, weight row 16 crb + r
@@ -214,14 +242,21 @@ __global__ __launch_bounds__(kF16Threads, 2) void gemv_f16_lds_kernel(
         if (f0 + p < F) compute(ring[p]);
 }
 
-template <int PF>
-hipError_t launch_f16_lds_t(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
-                            int64_t n, int64_t k, int Kp, int wps, int cu, hipStream_t stream) {
-    const size_t lds = (size_t)9 * Kp * 2;
+constexpr int kF16LdsMax = 160 * 1024;
+
+size_t f16_lds_bytes(int Kp) { return (size_t)9 * Kp * 2 + (size_t)kF16Waves * 2 * kTileBytes; }
+
+// Four steps in flight and two workgroups per CU where their LDS allows (a
+// sweep of 3..8 steps x 1..3 waves per SIMD on the 248,320-row heads).
+hipError_t launch_f16_lds(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
+                          int64_t n, int64_t k, int Kp, int cu, hipStream_t stream) {
+    constexpr int PF = 4;
+    const size_t lds = f16_lds_bytes(Kp);
     static std::atomic<uint64_t> lds_done{0};           // devices already set up
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_f16_lds_kernel<PF>),
                                      (int)lds, lds_done);
     if (e != hipSuccess) return e;
+    const int wps = 2 * lds <= (size_t)kF16LdsMax ? 2 : 1;
     const int64_t RB = (n + 15) / 16;
     const int64_t max_waves = (int64_t)cu * kF16Waves * wps;
     const int64_t per = (RB + max_waves - 1) / max_waves;
@@ -368,9 +403,8 @@ hipError_t launch_f16_m1(const uint16_t* x, const uint16_t* w, float* y, int64_t
 
 // m = 1: the streaming kernel where k fits it; otherwise (and for m = 2..8)
 // the MFMA kernel, with each wave owning a contiguous, balanced range of row
-// blocks: the LDS-staged form while 9 rows of padded k fit in 160 KB of LDS
-// (k <= 9088), from a sweep of steps in flight x waves per SIMD on the
-// 248,320-row heads: 4 steps x 2 waves up to k = 1536, 8 steps x 1 wave above.
+// blocks: the LDS form while its LDS fits in 160 KB (k <= 7168), else the
+// form that reads the activations from global memory.
 hipError_t launch_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
                            int64_t n, int64_t k, hipStream_t stream) {
     int dev = 0;
@@ -384,10 +418,8 @@ hipError_t launch_gemv_f16(const uint16_t* x, const uint16_t* w, float* y, int64
     }
     const int64_t steps = (k / 32 + kStepGroups - 1) / kStepGroups;
     const int64_t Kp = steps * 32 * kStepGroups;
-    if (9 * Kp * 2 <= 160 * 1024) {
-        if (k <= 1536) return launch_f16_lds_t<4>(x, w, y, m, n, k, (int)Kp, 2, cu, stream);
-        return launch_f16_lds_t<8>(x, w, y, m, n, k, (int)Kp, 1, cu, stream);
-    }
+    if (f16_lds_bytes((int)Kp) <= (size_t)kF16LdsMax)
+        return launch_f16_lds(x, w, y, m, n, k, (int)Kp, cu, stream);
     const int64_t RB = (n + 15) / 16;
     const int64_t max_waves = (int64_t)device_info(dev).cu_count * kF16Waves;
     const int64_t per = (RB + max_waves - 1) / max_waves;

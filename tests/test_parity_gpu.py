@@ -461,10 +461,11 @@ def test_gemv_topk_lm_head_full_size(q4, key, m, topk):
 # fp16 weights (q4_gemv_f16)
 # --------------------------------------------------------------------------
 
-# k = 9088 is the largest k whose padded activations (9 rows) fit the LDS of the m = 2..8
-# kernel; 9120 and 16416 take the kernel that reads them from global memory.
+# k = 7168 is the largest k for which the m = 2..8 kernel that stages the activations and
+# the weight tiles in LDS fits; 7200, 8192, 9120 and 16416 take the kernel that reads the
+# activations from global memory.
 F16_SHAPES = [(1, 32), (15, 64), (17, 96), (33, 256), (100, 1056), (257, 2560), (1024, 1024),
-              (5, 8192), (61, 4096), (4099, 128), (9, 9088), (9, 9120), (3, 16416)]
+              (5, 8192), (61, 4096), (4099, 128), (9, 7168), (9, 7200), (9, 9120), (3, 16416)]
 
 
 def _f16_case(m, n, k, seed):
