@@ -170,51 +170,97 @@ __device__ __forceinline__ void store_rows(float* __restrict__ y, const float (&
 }
 
 // Whole K in one LDS pass.  Each wave owns a contiguous, balanced range of
-// row blocks and streams it as one flat sequence of (row block, tile) steps;
+// row blocks and streams it as one flat sequence of (row block, step) steps;
 // the prefetch ring runs across row-block boundaries, so a wave's loads never
-// drain until its range is done.
-template <int TB, bool kScale16>
+// drain until its range is done.  A step is 16 rows x 16 groups (two tiles).
+// The codes are read in whole 256-byte row segments -- lane (lr, lj) =
+// (lane / 16, lane % 16) loads group 16 t + lj of row 4 i + lr, i < 4, so one
+// wave load covers 4 rows x 256 contiguous bytes, where a load in the tile
+// layout itself would cover 16 rows x 64 bytes (~5.3 TB/s for that pattern
+// alone) -- and each step passes through a wave-private LDS tile into the
+// per-lane tile layout: group j of row n at 256 n + 16 ((j + n) mod 16), a
+// rotation that keeps the row-wise writes and the tile reads (lane (n, kb)
+// reads groups 8 h + kb and 8 h + 4 + kb of row n) free of bank conflicts.
+// Lane (lane / 4, lane % 4) loads four of its row's 16 scales of the step;
+// the tile's eight scales of row n are read back as one 16-byte piece.  Two
+// step buffers per wave alternate.  The arithmetic (compute_tile) and the
+// order of every sum are those of the tile layout, so the results do not
+// depend on the load path.
+constexpr int kStepGroups = 16;
+constexpr int kStepCodeBytes = 16 * 256;
+constexpr int kStepBytes = kStepCodeBytes + 16 * 32;      // codes + scales of a step
+
+template <int TB, bool kWhole16>
 __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
                                           const uint8_t* __restrict__ packed,
                                           const uint16_t* __restrict__ scales,
-                                          float* __restrict__ y, _Float16* xs, int M,
-                                          int64_t N, int K, int G, int64_t RB,
-                                          const SpliceConsts& kc) {
+                                          float* __restrict__ y, _Float16* xs,
+                                          unsigned char* step_bufs, int M, int64_t N, int K,
+                                          int G, int64_t RB, const SpliceConsts& kc) {
     const int lane = threadIdx.x & 63;
-    const int kb = lane >> 4;
+    const int kb = lane >> 4, rr = lane & 15;             // tile layout
+    const int lr = lane >> 4, lj = lane & 15;             // code loads
+    const int sr = lane >> 2, sp = lane & 3;              // scale loads
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t W = (int64_t)gridDim.x * kGemvWaves;
-    const int64_t w = (int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6);
+    const int64_t w = (int64_t)blockIdx.x * kGemvWaves + wave;
     const int64_t base = RB / W, extra = RB % W;
     const int64_t rb_begin = w * base + (w < extra ? w : extra);
     const int64_t count = base + (w < extra ? 1 : 0);
-    const int T = ((G + 7) & ~7) / kTileGroups;          // tiles per row block
+    const int T = ((G + 15) & ~15) / kStepGroups;        // steps per row block
     const int64_t F = count * T;                         // flat steps of this wave
+    unsigned char* bufs = step_bufs + (size_t)wave * 2 * kStepBytes;
 
+    struct Step {
+        u32x4_t v[4];                                    // codes, row 4 i + lr, group lj
+        uint32_t s0, s1;                                 // scales 4 sp .. 4 sp + 3 of row sr
+    };
     // load cursor, advanced with selects rather than branches: with a
-    // branch-free loop body the compiler keeps the later tiles' loads in
-    // flight instead of waiting for every load at each tile (measured 7%
-    // faster on the M = 8 LM head).  Steps past the wave's range re-read row
-    // N-1 (see load_tile).
+    // branch-free loop body the compiler keeps the later steps' loads in
+    // flight instead of waiting for every load at each step.  Steps past the
+    // wave's range re-read row N-1; groups past G re-read group G-1 (their
+    // activations in LDS are zero).
     const int64_t rb_end = rb_begin + count;
     int64_t lrb = rb_begin;
     int lt = 0;
-    auto load_next = [&]() -> Tile {
-        const int64_t n = lrb * 16 + (lane & 15);
-        const int64_t nc = (lrb < rb_end && n < N) ? n : N - 1;
-        Tile t = load_tile<kScale16>(packed + nc * (int64_t)(K / 2), scales + nc * (int64_t)G,
-                                     lt * kTileGroups, kb, G);
+    auto load_next = [&]() -> Step {
+        Step st;
+        const int g = lt * kStepGroups + lj;
+        const int gc = g < G ? g : G - 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = lrb * 16 + 4 * i + lr;
+            const int64_t nc = (lrb < rb_end && n < N) ? n : N - 1;
+            st.v[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(packed + nc * (int64_t)(K / 2) + 16 * gc));
+        }
+        const int64_t ns = lrb * 16 + sr;
+        const int64_t nsc = (lrb < rb_end && ns < N) ? ns : N - 1;
+        const uint16_t* srow = scales + nsc * (int64_t)G;
+        const int gs = lt * kStepGroups + 4 * sp;
+        if (kWhole16) {                                  // G % 16 == 0: the step is whole
+            const uint2 v = *reinterpret_cast<const uint2*>(srow + gs);
+            st.s0 = v.x;
+            st.s1 = v.y;
+        } else {
+            uint32_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = srow[min(gs + e, G - 1)];
+            st.s0 = h[0] | (h[1] << 16);
+            st.s1 = h[2] | (h[3] << 16);
+        }
         const int nt = lt + 1;
         const bool wrap = nt == T;
         lt = wrap ? 0 : nt;
         lrb += wrap ? 1 : 0;
-        return t;
+        return st;
     };
 
-    Tile ring[kPrefetch];
+    Step ring[kPrefetch];
 #pragma unroll
     for (int p = 0; p < kPrefetch; ++p) ring[p] = load_next();
 
-    stage_x<TB>(x, xs, M, K, G, 0, T * kTileGroups);
+    stage_x<TB>(x, xs, M, K, G, 0, T * kStepGroups);
     __syncthreads();
 
     const uint32_t magic = to_vgpr(kc.magic);
@@ -223,9 +269,31 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[tb] = 0.f;
     int64_t crb = rb_begin;
-    int ct = 0;
-    const int cg = T * kTileGroups;
-    auto finish = [&]() {                       // after each tile: store a finished row block
+    int ct = 0, sel = 0;
+    const int cg = T * kStepGroups;
+    // one step: through the wave's LDS buffer (the wave's own LDS accesses
+    // are performed in order), then the two tiles; a finished row block is
+    // stored
+    auto compute_step = [&](const Step& st) {
+        unsigned char* buf = bufs + sel * kStepBytes;
+        sel ^= 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = 4 * i + lr;
+            *reinterpret_cast<u32x4_t*>(buf + 256 * n + 16 * ((lj + n) & 15)) = st.v[i];
+        }
+        *reinterpret_cast<uint2*>(buf + kStepCodeBytes + 32 * sr + 8 * sp) = uint2{st.s0, st.s1};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            Tile t;
+            t.p0 = *reinterpret_cast<const u32x4_t*>(buf + 256 * rr +
+                                                     16 * ((8 * h + kb + rr) & 15));
+            t.p1 = *reinterpret_cast<const u32x4_t*>(buf + 256 * rr +
+                                                     16 * ((8 * h + 4 + kb + rr) & 15));
+            t.sc = *reinterpret_cast<const u32x4_t*>(buf + kStepCodeBytes + 32 * rr + 16 * h);
+            compute_tile<TB>(t, xs, cg, ct * kStepGroups + 8 * h, lane, kc.mask, kc.mask16,
+                             magic, a, acc);
+        }
         if (++ct == T) {
             store_rows<TB>(y, acc, crb, lane, M, N);
 #pragma unroll
@@ -234,25 +302,18 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
             ++crb;
         }
     };
-    // full rounds of kPrefetch tiles, then the last tiles with no new loads
+    // full rounds of kPrefetch steps, then the last steps with no new loads
     int64_t f0 = 0;
     for (; f0 + kPrefetch < F; f0 += kPrefetch) {
 #pragma unroll
         for (int p = 0; p < kPrefetch; ++p) {
-            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, kc.mask, kc.mask16,
-                             magic, a, acc);
+            compute_step(ring[p]);
             ring[p] = load_next();
-            finish();
         }
     }
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p) {
-        if (f0 + p < F) {
-            compute_tile<TB>(ring[p], xs, cg, ct * kTileGroups, lane, kc.mask, kc.mask16,
-                             magic, a, acc);
-            finish();
-        }
-    }
+    for (int p = 0; p < kPrefetch; ++p)
+        if (f0 + p < F) compute_step(ring[p]);
 }
 
 // K larger than one LDS pass: activations are staged chunk by chunk, with
@@ -313,51 +374,86 @@ __device__ __forceinline__ void gemv_chunked(const uint16_t* __restrict__ x,
     }
 }
 
+template <int TB, bool kWhole16>
+__global__ __launch_bounds__(kGemvThreads, 2) void gemv_flat_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scales, float* __restrict__ y, int M, int64_t N, int K,
+    int G, int64_t RB, int xs_bytes, SpliceConsts kc) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    gemv_flat<TB, kWhole16>(x, packed, scales, y, reinterpret_cast<_Float16*>(smem),
+                            smem + xs_bytes, M, N, K, G, RB, kc);
+}
+
 template <int TB, bool kScale16>
 __global__ __launch_bounds__(kGemvThreads, 2) void gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, float* __restrict__ y, int M, int64_t N, int K,
     int G, int chunk_groups, int nchunks, int64_t RB, SpliceConsts kc) {
     extern __shared__ __align__(16) unsigned char smem[];
-    _Float16* xs = reinterpret_cast<_Float16*>(smem);
-    if (nchunks == 1)
-        gemv_flat<TB, kScale16>(x, packed, scales, y, xs, M, N, K, G, RB, kc);
-    else
-        gemv_chunked<TB, kScale16>(x, packed, scales, y, xs, M, N, K, G, chunk_groups, nchunks,
-                                   RB, kc);
+    gemv_chunked<TB, kScale16>(x, packed, scales, y, reinterpret_cast<_Float16*>(smem), M, N, K,
+                               G, chunk_groups, nchunks, RB, kc);
 }
 
-template <int TB, bool kScale16>
+// Whole K staged at once when the padded activations and 2 step buffers per
+// wave fit the CU's 160 KB of LDS (k <= 7680 at m = 5..8, 15360 at m <= 4):
+// two workgroups per CU where their LDS allows (measured faster than one at
+// k = 1024 and 2560), each wave with the same number of row blocks.
+// Otherwise chunked (kLdsBudget of activations per pass), as many waves as fit.
+template <int TB>
 hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
                          const uint16_t* scales, float* y, int m, int64_t n,
                          int k, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    const int cu = device_info(dev).cu_count;
     const int G = k / 32;
-    const int gpad = (G + 7) & ~7;
     const int per_group_bytes = TB * 4 * 64;
     const int fixed_bytes = TB * 4 * kTokenPad * 2 + 64;     // token pads, zero block
+    const int64_t RB = (n + 15) / 16;
+    const int64_t g16 = (G + 15) & ~15;
+    const int64_t xs_bytes = (per_group_bytes * g16 + fixed_bytes + 15) & ~15;
+    const size_t lds = (size_t)xs_bytes + (size_t)kGemvWaves * 2 * kStepBytes;
+    if (lds <= (size_t)160 * 1024) {
+        const int wgs = 2 * lds <= (size_t)160 * 1024 ? 2 : 1;
+        const int64_t max_waves = (int64_t)cu * kGemvWaves * wgs;
+        const int64_t per = (RB + max_waves - 1) / max_waves;
+        const int64_t waves = (RB + per - 1) / per;
+        const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
+        const bool whole = G % 16 == 0;
+        const void* fn = whole ? reinterpret_cast<const void*>(&gemv_flat_kernel<TB, true>)
+                               : reinterpret_cast<const void*>(&gemv_flat_kernel<TB, false>);
+        static std::atomic<uint64_t> lds_done[2] = {{0}, {0}};
+        e = allow_dynamic_lds(fn, (int)lds, lds_done[whole ? 1 : 0]);
+        if (e != hipSuccess) return e;
+        if (whole)
+            hipLaunchKernelGGL((gemv_flat_kernel<TB, true>), dim3(blocks), dim3(kGemvThreads), lds,
+                               stream, x, packed, scales, y, m, n, k, G, RB, (int)xs_bytes,
+                               kSpliceConsts);
+        else
+            hipLaunchKernelGGL((gemv_flat_kernel<TB, false>), dim3(blocks), dim3(kGemvThreads),
+                               lds, stream, x, packed, scales, y, m, n, k, G, RB, (int)xs_bytes,
+                               kSpliceConsts);
+        return hipGetLastError();
+    }
+    const int gpad = (G + 7) & ~7;
     int chunk = ((kLdsBudget - fixed_bytes) / per_group_bytes) & ~7;
     if (chunk > gpad) chunk = gpad;
     const int nchunks = (gpad + chunk - 1) / chunk;
-    const int64_t RB = (n + 15) / 16;
     // resident waves: 4 per SIMD, 4 SIMDs per CU
-    const int64_t max_waves = (int64_t)device_info(dev).cu_count * 16;
-    int64_t waves;
-    if (nchunks == 1) {
-        // as many waves as fit, then trimmed so that every wave gets the same
-        // number of row blocks (ceil(RB / waves) blocks each)
-        const int64_t per = (RB + max_waves - 1) / max_waves;
-        waves = (RB + per - 1) / per;
-    } else {
-        waves = RB < max_waves ? RB : max_waves;
-    }
+    const int64_t max_waves = (int64_t)cu * 16;
+    const int64_t waves = RB < max_waves ? RB : max_waves;
     const int64_t blocks64 = (waves + kGemvWaves - 1) / kGemvWaves;
     const int blocks = (int)(blocks64 > 0 ? blocks64 : 1);
-    const size_t lds = (size_t)per_group_bytes * chunk + fixed_bytes;
-    hipLaunchKernelGGL((gemv_kernel<TB, kScale16>), dim3(blocks), dim3(kGemvThreads), lds,
-                       stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB, kSpliceConsts);
+    const size_t chunk_lds = (size_t)per_group_bytes * chunk + fixed_bytes;
+    if (G % 8 == 0)
+        hipLaunchKernelGGL((gemv_kernel<TB, true>), dim3(blocks), dim3(kGemvThreads), chunk_lds,
+                           stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB,
+                           kSpliceConsts);
+    else
+        hipLaunchKernelGGL((gemv_kernel<TB, false>), dim3(blocks), dim3(kGemvThreads), chunk_lds,
+                           stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB,
+                           kSpliceConsts);
     return hipGetLastError();
 }
 
@@ -649,12 +745,8 @@ hipError_t launch_gemv1(const uint16_t* x, int k, int count, const uint8_t* cons
 hipError_t launch_gemv_blockdiag(const uint16_t* x, const uint8_t* packed,
                                  const uint16_t* scales, float* y, int64_t m, int64_t n,
                                  int64_t k, hipStream_t stream) {
-    const bool s16 = ((k / 32) % 8) == 0;
-    if (m <= 4)
-        return s16 ? launch_gemv_t<1, true>(x, packed, scales, y, (int)m, n, (int)k, stream)
-                   : launch_gemv_t<1, false>(x, packed, scales, y, (int)m, n, (int)k, stream);
-    return s16 ? launch_gemv_t<2, true>(x, packed, scales, y, (int)m, n, (int)k, stream)
-               : launch_gemv_t<2, false>(x, packed, scales, y, (int)m, n, (int)k, stream);
+    if (m <= 4) return launch_gemv_t<1>(x, packed, scales, y, (int)m, n, (int)k, stream);
+    return launch_gemv_t<2>(x, packed, scales, y, (int)m, n, (int)k, stream);
 }
 
 }  // namespace

@@ -162,6 +162,19 @@ def test_prefill_product(q4, orc, m, n, k):
     assert_within(y, y_ref, bound, "q4_gemm m=%d n=%d k=%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m,k", [(4, 15360), (4, 15392), (8, 7680), (8, 7712), (5, 1504),
+                                 (2, 4160)])
+@pytest.mark.parametrize("n", [5, 4099])
+def test_blockdiag_lds_limits(q4, orc, m, n, k):
+    """m = 2..8 at the largest k whose activations and step buffers fit in LDS
+    (15360 for m <= 4, 7680 for m = 5..8) and just past it (chunked kernel),
+    and k whose group count is not a multiple of the 16 groups of a step."""
+    x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m * 7 + n + k)
+    _log("q4_gemv m=%d n=%d k=%d" % (m, n, k))
+    y = product(q4, "q4_gemv", x, packed, scales)
+    assert_within(y, y_ref, bound, "q4_gemv m=%d n=%d k=%d" % (m, n, k))
+
+
 @pytest.mark.parametrize("fn,m,k", [("q4_gemv", 1, 65536), ("q4_gemv", 8, 65536),
                                     ("q4_gemm", 40, 65536), ("q4_gemv", 1, 2 ** 20)])
 def test_long_k(q4, orc, fn, m, k):
