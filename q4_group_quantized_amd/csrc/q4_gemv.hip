@@ -29,7 +29,8 @@
 // Activations are staged once per workgroup in LDS, permuted inside every
 // 8-element chunk to the order unpack8_fma produces codes in, so A and B agree
 // element by element.  Scales are read as 8 consecutive fp16 per lane (one
-// 16-byte load when the scale rows are 16-byte aligned).
+// 16-byte load when G % 8 == 0 and the scale matrix is 16-byte aligned, else
+// eight 2-byte loads).
 //
 // m = 1 has its own streaming kernel (gemv1_kernel below): there the block-
 // diagonal MFMA would waste 15/16 of the matrix core anyway, and what bounds
@@ -79,7 +80,7 @@ __device__ __forceinline__ Tile load_tile(const uint8_t* __restrict__ prow,
     const int ja = min(j0 + kb, G - 1), jb = min(j0 + 4 + kb, G - 1);
     t.p0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(prow + 16 * ja));
     t.p1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(prow + 16 * jb));
-    if (kScale16) {                              // G % 8 == 0: the tile is whole
+    if (kScale16) {                              // G % 8 == 0 and 16-byte aligned scales
         t.sc = *reinterpret_cast<const u32x4_t*>(srow + j0);
     } else {
         uint32_t h[8];
@@ -238,7 +239,7 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
         const int64_t nsc = (lrb < rb_end && ns < N) ? ns : N - 1;
         const uint16_t* srow = scales + nsc * (int64_t)G;
         const int gs = lt * kStepGroups + 4 * sp;
-        if (kWhole16) {                                  // G % 16 == 0: the step is whole
+        if (kWhole16) {                   // G % 16 == 0 (whole step), 8-byte aligned scales
             const uint2 v = *reinterpret_cast<const uint2*>(srow + gs);
             st.s0 = v.x;
             st.s1 = v.y;
@@ -420,7 +421,9 @@ hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
         const int64_t per = (RB + max_waves - 1) / max_waves;
         const int64_t waves = (RB + per - 1) / per;
         const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
-        const bool whole = G % 16 == 0;
+        // 8-byte scale loads need whole steps and an 8-byte aligned scale
+        // matrix (the contract only promises 2 bytes)
+        const bool whole = G % 16 == 0 && (reinterpret_cast<uintptr_t>(scales) & 7) == 0;
         const void* fn = whole ? reinterpret_cast<const void*>(&gemv_flat_kernel<TB, true>)
                                : reinterpret_cast<const void*>(&gemv_flat_kernel<TB, false>);
         static std::atomic<uint64_t> lds_done[2] = {{0}, {0}};
@@ -446,7 +449,7 @@ hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
     const int64_t blocks64 = (waves + kGemvWaves - 1) / kGemvWaves;
     const int blocks = (int)(blocks64 > 0 ? blocks64 : 1);
     const size_t chunk_lds = (size_t)per_group_bytes * chunk + fixed_bytes;
-    if (G % 8 == 0)
+    if (G % 8 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)   // 16-byte scale loads
         hipLaunchKernelGGL((gemv_kernel<TB, true>), dim3(blocks), dim3(kGemvThreads), chunk_lds,
                            stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB,
                            kSpliceConsts);

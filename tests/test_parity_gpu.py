@@ -175,6 +175,34 @@ def test_blockdiag_lds_limits(q4, orc, m, n, k):
     assert_within(y, y_ref, bound, "q4_gemv m=%d n=%d k=%d" % (m, n, k))
 
 
+SCALE_OFFSET_CASES = [("q4_gemv", 1, 1024), ("q4_gemv", 2, 1024), ("q4_gemv", 5, 544),
+                      ("q4_gemv", 8, 7936), ("q4_gemv", 3, 16384), ("q4_gemm", 40, 1024)]
+
+
+@pytest.mark.parametrize("fn,m,k", SCALE_OFFSET_CASES,
+                         ids=["%s-m%d-k%d" % c for c in SCALE_OFFSET_CASES])
+@pytest.mark.parametrize("offset", [1, 2, 4, 8])
+def test_scales_at_any_even_address(q4, orc, fn, m, k, offset):
+    """The scale matrix need only be 2-byte aligned: it is placed `offset`
+    fp16 elements past a 256-byte boundary (2, 4, 8 and 16 bytes), so the
+    kernels whose wide scale loads need 8 or 16 bytes (m = 2..8 with a whole
+    number of steps or tiles) must take their 2-byte form there.  Every
+    offset gives the bits of the aligned call."""
+    n = 37
+    x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m + k + offset)
+    _log("%s m=%d n=%d k=%d scales at +%d B" % (fn, m, n, k, 2 * offset))
+    y0 = product(q4, fn, x, packed, scales)
+    buf = torch.zeros(scales.size + 16, dtype=torch.float16, device=DEV)
+    shifted = buf[offset:offset + scales.size].view(scales.shape)
+    shifted.copy_(gpu(scales.view(np.float16)))
+    assert shifted.data_ptr() % 256 == 2 * offset
+    y = getattr(q4, fn)(gpu(x), gpu(packed), shifted)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), y0.astype(np.float32).view(np.uint32))
+    assert_within(y.astype(np.float64), y_ref, bound, "%s scales at +%d B" % (fn, 2 * offset))
+
+
 @pytest.mark.parametrize("fn,m,k", [("q4_gemv", 1, 65536), ("q4_gemv", 8, 65536),
                                     ("q4_gemm", 40, 65536), ("q4_gemv", 1, 2 ** 20)])
 def test_long_k(q4, orc, fn, m, k):
