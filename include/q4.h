@@ -197,7 +197,9 @@ q4_status q4_gemv_topk(const uint16_t* x, const uint8_t* packed,
  * q4_gemm -- prefill product, same arguments and semantics as q4_gemv, for
  * any m in 1 .. 2^31-1 (tuned for m >= 16): all projections of a token batch
  * computed at once, as in the QORA-4B article's GPU prefill section and the
- * batched prefill of the QORA-LLM-0.8B card ("Performance").
+ * batched prefill of the QORA-LLM-0.8B card ("Performance").  m <= 8 runs
+ * q4_gemv.  The result is deterministic for a given (m, n, k) on a given
+ * device model (the tile shape follows m, n and the number of CUs).
  */
 q4_status q4_gemm(const uint16_t* x, const uint8_t* packed,
                   const uint16_t* scales, float* y,
@@ -208,8 +210,11 @@ q4_status q4_gemm(const uint16_t* x, const uint8_t* packed,
  * one launch: all projections that read one input during prefill (QORA-4B
  * article, GPU prefill section: the projections of a token batch computed
  * together on the GPU).  Arguments as q4_gemv_multi, with any m >= 1 (m <= 8
- * takes the q4_gemv_multi path).  Each y[i] is bit-identical to what q4_gemm
- * returns for matrix i alone.
+ * takes the q4_gemv_multi path, whose outputs are bit-identical to q4_gemv's).
+ * Each y[i] meets q4_gemm's accuracy bound and is deterministic for a given
+ * set of shapes; for m > 32 the launch picks its tile shape from the tiles of
+ * all its matrices, so y[i] may differ from q4_gemm on matrix i alone in the
+ * last bits (the order of the fp32 sums follows the tile shape).
  */
 q4_status q4_gemm_multi(const uint16_t* x, int64_t m, int64_t k, int32_t count,
                         const uint8_t* const* packed, const uint16_t* const* scales,

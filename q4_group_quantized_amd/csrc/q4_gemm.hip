@@ -17,7 +17,9 @@
 // all BM rows and 32 columns over G/WK groups, so every code is unpacked by
 // exactly one wave and every activation is read from LDS by WN waves.  The
 // WK partial tiles are added in LDS at the end in a fixed order
-// (deterministic).
+// (deterministic).  The tile shape is chosen per launch from m and the number
+// of tiles of all its matrices (choose_tile); the order of the fp32 sums, and
+// so the last bits of a result, depend on that shape.
 //
 // Data movement.  Every operand goes straight from global memory into LDS
 // with direct-to-LDS loads, through an S-stage ring per K slice:
@@ -79,8 +81,8 @@ struct Gemm {
 // The matrices of one launch: up to kGemmMaxSegments weight matrices over the
 // same activations (one for q4_gemm).  Segment s owns workgroups
 // [tile0[s], tile0[s] + tiles[s]); a tile's work and its order of fp32 sums
-// depend only on its index inside its segment, so every matrix gets the
-// result a launch of its own would give, bit for bit.
+// depend only on its index inside its segment and on the launch's tile shape,
+// never on the other matrices of the launch.
 constexpr int kGemmMaxSegments = 8;
 struct GemmSegments {
     const uint8_t* packed[kGemmMaxSegments];
@@ -342,6 +344,41 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
     return hipGetLastError();
 }
 
+// Tile shapes for m > 32 and the time one round of them takes (every CU one
+// tile, k = 2560, measured in microseconds; only the ratios matter, and they
+// hold for any k since every tile walks all of K).
+struct TileChoice {
+    int bm, bn;
+    float round_us;
+};
+constexpr TileChoice kTiles[] = {
+    {128, 128, 35.f},      // gemm_kernel<128, 4, 2, 2, 2>
+    {64, 128, 23.f},       // gemm_kernel<64, 4, 2, 2, 2>
+    {64, 64, 15.5f},       // gemm_kernel<64, 2, 4, 2, 2>
+    {32, 64, 11.f},        // gemm_kernel<32, 2, 4, 2, 2>
+};
+
+// The tile shape whose estimated time -- rounds of tiles over the CUs times
+// the round time -- is least for this launch (ties to the larger tile): the
+// largest tiles move the fewest operand bytes per output, but too few of them
+// leave CUs idle.  The estimate counts the tiles of every matrix of the launch.
+int choose_tile(int64_t m, int count, const int64_t* n, int cu_count) {
+    int best = 0;
+    double best_us = 0.0;
+    for (int c = 0; c < (int)(sizeof(kTiles) / sizeof(kTiles[0])); ++c) {
+        int64_t tiles = 0;
+        for (int i = 0; i < count; ++i) tiles += (n[i] + kTiles[c].bn - 1) / kTiles[c].bn;
+        tiles *= (m + kTiles[c].bm - 1) / kTiles[c].bm;
+        const int64_t rounds = (tiles + cu_count - 1) / cu_count;
+        const double us = (double)rounds * kTiles[c].round_us;
+        if (c == 0 || us < best_us) {
+            best = c;
+            best_us = us;
+        }
+    }
+    return best;
+}
+
 hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* const* packed,
                                 const uint16_t* const* scales, float* const* y,
                                 const int64_t* n, int64_t m, int64_t k, hipStream_t stream) {
@@ -349,13 +386,15 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
         return launch_gemm_t<16, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
     if (m <= 32)
         return launch_gemm_t<32, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
-    if (m < 256)
-        return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
-    if (m < 1024)
-        return launch_gemm_t<128, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
-    // from 1024 rows on, 128 x 128 tiles still give every CU a tile and halve
-    // the activation traffic per output (measured 15% faster at M = 2048)
-    return launch_gemm_t<128, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    switch (choose_tile(m, count, n, device_info(dev).cu_count)) {
+        case 0: return launch_gemm_t<128, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+        case 1: return launch_gemm_t<64, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+        case 2: return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+        default: return launch_gemm_t<32, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+    }
 }
 
 }  // namespace
