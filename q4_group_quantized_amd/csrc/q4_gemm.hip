@@ -344,40 +344,14 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
     return hipGetLastError();
 }
 
-// Tile shapes for m > 32 and the time one round of them takes (every CU one
-// tile, k = 2560, measured in microseconds; only the ratios matter, and they
-// hold for any k since every tile walks all of K).
-struct TileChoice {
-    int bm, bn;
-    float round_us;
-};
+// Tile shapes for m > 32, largest first, with the time one full round of
+// them takes (k = 2560, n = 4096, one tile per CU; measured).
 constexpr TileChoice kTiles[] = {
     {128, 128, 35.f},      // gemm_kernel<128, 4, 2, 2, 2>
     {64, 128, 23.f},       // gemm_kernel<64, 4, 2, 2, 2>
     {64, 64, 15.5f},       // gemm_kernel<64, 2, 4, 2, 2>
     {32, 64, 11.f},        // gemm_kernel<32, 2, 4, 2, 2>
 };
-
-// The tile shape whose estimated time -- rounds of tiles over the CUs times
-// the round time -- is least for this launch (ties to the larger tile): the
-// largest tiles move the fewest operand bytes per output, but too few of them
-// leave CUs idle.  The estimate counts the tiles of every matrix of the launch.
-int choose_tile(int64_t m, int count, const int64_t* n, int cu_count) {
-    int best = 0;
-    double best_us = 0.0;
-    for (int c = 0; c < (int)(sizeof(kTiles) / sizeof(kTiles[0])); ++c) {
-        int64_t tiles = 0;
-        for (int i = 0; i < count; ++i) tiles += (n[i] + kTiles[c].bn - 1) / kTiles[c].bn;
-        tiles *= (m + kTiles[c].bm - 1) / kTiles[c].bm;
-        const int64_t rounds = (tiles + cu_count - 1) / cu_count;
-        const double us = (double)rounds * kTiles[c].round_us;
-        if (c == 0 || us < best_us) {
-            best = c;
-            best_us = us;
-        }
-    }
-    return best;
-}
 
 hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* const* packed,
                                 const uint16_t* const* scales, float* const* y,
@@ -389,7 +363,7 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
     int dev = 0;
     const hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    switch (choose_tile(m, count, n, device_info(dev).cu_count)) {
+    switch (choose_tile(kTiles, 4, m, count, n, device_info(dev).cu_count)) {
         case 0: return launch_gemm_t<128, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
         case 1: return launch_gemm_t<64, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
         case 2: return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);

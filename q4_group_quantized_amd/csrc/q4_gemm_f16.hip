@@ -249,14 +249,25 @@ hipError_t launch_gemm_f16(const uint16_t* x, const uint16_t* w, float* y, int64
     if (m <= 8) return launch_gemv_f16(x, w, y, m, n, k, stream);
     if (m <= 16) return launch_gemm_f16_t<16, 1, 4, 2, 4>(x, w, y, m, n, k, stream);
     if (m <= 32) return launch_gemm_f16_t<32, 1, 4, 2, 4>(x, w, y, m, n, k, stream);
-    if (m < 256) return launch_gemm_f16_t<64, 2, 4, 2, 2>(x, w, y, m, n, k, stream);
-    if (m < 512) return launch_gemm_f16_t<128, 2, 4, 1, 3>(x, w, y, m, n, k, stream);
-    // wider tiles without a K split once every CU still gets one: with 3.6x
-    // the weight bytes of Q4, fewer weight re-reads per output pay (measured
-    // at K = 2560, N = 4096: 28.1 against 34.5 us at M = 512, 96.7 against
-    // 126 us at M = 2048)
-    if (m < 1024) return launch_gemm_f16_t<64, 4, 1, 2, 4>(x, w, y, m, n, k, stream);
-    return launch_gemm_f16_t<128, 4, 1, 1, 8>(x, w, y, m, n, k, stream);
+    // above, the tile shape with the least estimated time (choose_tile); the
+    // 128- and 64-column-wide shapes without a K split pay with 3.6x the weight
+    // bytes of Q4 (fewer weight re-reads per output).  Round times measured
+    // at k = 2560, n = 4096, one tile per CU.
+    static constexpr TileChoice kTilesF16[] = {
+        {128, 128, 38.5f},     // gemm_f16_kernel<128, 4, 1, 1, 8>
+        {64, 128, 23.6f},      // gemm_f16_kernel<64, 4, 1, 2, 4>
+        {64, 64, 19.6f},       // gemm_f16_kernel<64, 2, 4, 2, 2>
+        {32, 64, 16.2f},       // gemm_f16_kernel<32, 2, 4, 2, 2>
+    };
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    switch (choose_tile(kTilesF16, 4, m, 1, &n, device_info(dev).cu_count)) {
+        case 0: return launch_gemm_f16_t<128, 4, 1, 1, 8>(x, w, y, m, n, k, stream);
+        case 1: return launch_gemm_f16_t<64, 4, 1, 2, 4>(x, w, y, m, n, k, stream);
+        case 2: return launch_gemm_f16_t<64, 2, 4, 2, 2>(x, w, y, m, n, k, stream);
+        default: return launch_gemm_f16_t<32, 2, 4, 2, 2>(x, w, y, m, n, k, stream);
+    }
 }
 
 }  // namespace q4

@@ -25,6 +25,35 @@ bool device_usable(int device);
 // from several threads.
 hipError_t allow_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done);
 
+// A GEMM tile shape and the time (microseconds, measured at k = 2560) one
+// round of it takes when every CU runs one tile; only the ratios matter.
+struct TileChoice {
+    int bm, bn;
+    float round_us;
+};
+
+// Index of the shape in `tiles` whose estimated time -- rounds of tiles over
+// the CUs times its round time -- is least for m rows and the column counts
+// n[0..count) (ties to the earlier entry: list the larger tiles first).
+// Large tiles move the fewest operand bytes per output; too few of them
+// leave CUs idle.
+inline int choose_tile(const TileChoice* tiles, int ntiles, int64_t m, int count,
+                       const int64_t* n, int cu_count) {
+    int best = 0;
+    double best_us = 0.0;
+    for (int c = 0; c < ntiles; ++c) {
+        int64_t t = 0;
+        for (int i = 0; i < count; ++i) t += (n[i] + tiles[c].bn - 1) / tiles[c].bn;
+        t *= (m + tiles[c].bm - 1) / tiles[c].bm;
+        const double us = (double)((t + cu_count - 1) / cu_count) * tiles[c].round_us;
+        if (c == 0 || us < best_us) {
+            best = c;
+            best_us = us;
+        }
+    }
+    return best;
+}
+
 hipError_t launch_quantize(const float* w, uint8_t* packed, uint16_t* scales,
                            int64_t n, int64_t k, hipStream_t stream);
 

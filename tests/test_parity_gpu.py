@@ -634,6 +634,25 @@ def test_gemm_f16_product(q4, orc, m, n, k):
                   "q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
 
 
+F16_TILING_CASES = [(64, 1000, 256), (256, 4096, 256), (384, 4096, 128), (768, 4100, 96),
+                    (1030, 4100, 96)]
+
+
+@pytest.mark.parametrize("m,n,k", F16_TILING_CASES,
+                         ids=["m%d-n%d-k%d" % c for c in F16_TILING_CASES])
+def test_gemm_f16_every_tile_shape(q4, orc, m, n, k):
+    """Shapes for which the fp16-weight GEMM picks each of its tile shapes on a
+    256-CU device (32x64, 64x64, 64x128, 128x128, and 64x128 with ragged rows
+    and columns), compared in full."""
+    x, w = _f16_case(m, n, k, seed=m + n + k)
+    _log("q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
+    y = q4.q4_gemm_f16(gpu(x), gpu(w))
+    torch.cuda.synchronize()
+    y_ref, bound = orc.matmul_f16(x, w)
+    assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound,
+                  "q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
+
+
 def test_gemm_f16_exact_special_inputs(q4):
     """One-hot activation rows pick weight columns exactly; zero operands give zeros."""
     rng = np.random.default_rng(79)
