@@ -26,7 +26,9 @@
 //   activations  16 rows x 64 bytes of one group per wave instruction (1 KiB);
 //                each lane reads its A operand with one ds_read_b128
 //   codes        one whole 16-byte group of 64 columns per instruction
-//                (two instructions per group for 128-column tiles)
+//                (two instructions per group for 128-column tiles; 32-column
+//                tiles take two groups of their own 32 columns instead, so
+//                no lane loads a neighbouring tile's codes)
 //   scales       one fp16 per column, each landing in a 4-byte LDS slot
 // so the loop body issues no register-destination global loads and the only
 // waits on global memory are the explicit per-stage vmcnt waits below.
@@ -55,13 +57,18 @@ struct Gemm {
     static constexpr int MB = BM / 16;                     // 16-row blocks per wave
     static constexpr int BN = 32 * WN;
     static constexpr int H = (BN + 63) / 64;                         // 64-column code blocks
+    // 32-column tiles load the codes and scales of two groups per instruction
+    // (lanes 0-31 and 32-63); 64-column blocks take one group per instruction
+    static constexpr bool kPair = BN == 32;
+    static constexpr int kItems = kPair ? (KG + 1) / 2 : KG * H;    // code blocks per stage
     static constexpr int kCodeOff = KG * MB * kBlockBytes;           // within a stage
-    static constexpr int kScaleOff = kCodeOff + KG * H * kBlockBytes;
-    static constexpr int kStageBytes = kScaleOff + KG * H * 256;     // per K slice
+    static constexpr int kScaleOff = kCodeOff + kItems * kBlockBytes;
+    static constexpr int kStageBytes = kScaleOff + kItems * 256;     // per K slice
     static constexpr int kABlocksPerWave = KG * MB / WN;
-    // codes + scales of item i = (group i / H, 64-column block i % H) are
-    // loaded by wave i % WN of the K slice
-    static constexpr int groups_of(int wn) { return (KG * H - wn + WN - 1) / WN; }
+    // code block i of a stage (with its scales) is loaded by wave i % WN of
+    // the K slice: group i / H, 64-column block i % H -- or, paired, groups
+    // 2i and 2i + 1 of the tile's 32 columns
+    static constexpr int groups_of(int wn) { return wn < WN ? (kItems - wn + WN - 1) / WN : 0; }
     static constexpr int loads_per_stage(int wn) { return kABlocksPerWave + 2 * groups_of(wn); }
     static constexpr int kLdsBytes = WK * S * kStageBytes;
     // zeros that the operand reads of out-of-range groups are pointed at
@@ -162,6 +169,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const uint8_t* code_row1 = packed + ld_col1 * (K / 2);
     const uint16_t* scale_row0 = scales + ld_col0 * G;
     const uint16_t* scale_row1 = scales + ld_col1 * G;
+    // paired layout: lane = column (lane % 32) of group 2i + lane / 32
+    const int64_t pr_col = min<int64_t>(nt0 + (lane & 31), N - 1);
+    const uint8_t* code_rowp = packed + pr_col * (K / 2);
+    const uint16_t* scale_rowp = scales + pr_col * G;
+    const int pr_g = lane >> 5;
     // operand-side lane mapping
     const int col = lane & 15, kq = lane >> 4;
 
@@ -177,6 +189,19 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
             __builtin_amdgcn_global_load_lds(x + r * K + 32 * g + 8 * a_part,
                                              (lds_void_t*)(sb + (gl * MB + mb) * kBlockBytes),
                                              16, 0, 0);
+        }
+        if constexpr (C::kPair) {
+#pragma unroll
+            for (int it = 0; it < C::kItems; ++it) {
+                const int g = min(gs + 2 * it + pr_g, G - 1);
+                __builtin_amdgcn_global_load_lds(code_rowp + 16 * g,
+                                                 (lds_void_t*)(sb + C::kCodeOff + it * kBlockBytes),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(scale_rowp + g,
+                                                 (lds_void_t*)(sb + C::kScaleOff + it * 256), 2,
+                                                 0, 0);
+            }
+            return;
         }
 #pragma unroll
         for (int it = 0; it < KG * C::H; ++it) {
@@ -214,7 +239,9 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     };
     auto read_ops = [&](Ops& o, const unsigned char* sb, int gl, bool valid) {
         const unsigned char* ab = valid ? sb + gl * MB * kBlockBytes : zero;
-        const unsigned char* scb = valid ? sb + C::kScaleOff + gl * C::H * 256 : zero;
+        const int item = C::kPair ? gl >> 1 : gl * C::H;            // first code block of group gl
+        const int e0 = C::kPair ? 32 * (gl & 1) : 0;                   // its first entry there
+        const unsigned char* scb = valid ? sb + C::kScaleOff + item * 256 : zero;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
             o.a[mb] = *reinterpret_cast<const half8_t*>(ab + mb * kBlockBytes + 64 * col + 16 * kq);
@@ -222,8 +249,8 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
         for (int nb = 0; nb < 2; ++nb) {
             const int c = 32 * wn + 16 * nb + col;
             o.code[nb] = *reinterpret_cast<const uint32_t*>(
-                sb + C::kCodeOff + gl * C::H * kBlockBytes + 16 * c + 4 * kq);
-            o.sc[nb] = *reinterpret_cast<const _Float16*>(scb + 4 * c);
+                sb + C::kCodeOff + item * kBlockBytes + 16 * (e0 + c) + 4 * kq);
+            o.sc[nb] = *reinterpret_cast<const _Float16*>(scb + 4 * (e0 + c));
         }
     };
     auto compute = [&](const Ops& o) {
