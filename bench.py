@@ -31,7 +31,10 @@ detail   = the other halves of the hot path measured in the same run: the 4B
            in one q4_gemm_multi launch (against six q4_gemm launches) (TFLOP/s against the
            2.5 PFLOP/s dense fp16 MFMA peak) and the quantizer (GB/s); --all
            adds the 4B decode set, the M = 8 verify LM head and the
-           M = 16/128/2048 prefill GEMMs
+           M = 16/128/2048 prefill GEMMs.  The GEMMs, the verify head and the
+           fp16-weight products are timed as back-to-back launches replayed
+           from a HIP graph (after ~20 ms of replays), so host launch cost
+           does not pace them
 cpu_baseline = the CPU oracle (plain C, fp64 product) on a bounded sample of
            the same decode set, GB/s over the same algorithmic bytes
 
@@ -407,9 +410,32 @@ def graph_rate(torch, lib, fn, prod, launches, replays):
     torch.cuda.synchronize()
     if not torch.equal(prod.y, eager):
         raise RuntimeError("%s graph differs from the eager launch" % fn)
-    for _ in range(3):
+    settle(torch, lambda i: g.replay())
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
         g.replay()
+    b.record()
     torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (replays * launches) / 1e3
+
+
+def graph_time(torch, go, launches, replays):
+    """Per-call duration (s) of go(i, stream) for i < launches, captured in one
+    HIP graph after an eager call outside the capture, timed over `replays`
+    replays that follow ~SETTLE_S of replays."""
+    go(0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(launches):
+            go(i, h)
+    torch.cuda.synchronize()
+    settle(torch, lambda i: g.replay())
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(replays):
@@ -455,28 +481,21 @@ def lm_head_rate(torch, q4, lib, mat, iters):
 
 
 def f16_gemv_rate(torch, q4, lib, mat, m, iters, fn="q4_gemv_f16", outliers=False):
-    """Back-to-back q4_gemv_f16 (or q4_gemm_f16) launches over rotated fp16 weight copies."""
+    """Back-to-back q4_gemv_f16 (or q4_gemm_f16) launches over rotated fp16 weight
+    copies, replayed from a HIP graph."""
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
     w0 = torch.from_numpy(qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)).cuda().half()
     copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 2)))
     ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     y = torch.empty((m, mat.n), dtype=torch.float32, device=x.device)
-    sh = torch.cuda.current_stream().cuda_stream
     call = getattr(lib, fn)
 
-    def go(i):
+    def go(i, sh):
         st = call(x.data_ptr(), ws[i % copies].data_ptr(), y.data_ptr(), m, mat.n, mat.k, sh)
         if st != 0:
             raise RuntimeError("%s failed with status %d" % (fn, st))
-    settle(torch, go)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(iters):
-        go(i)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / iters / 1e3
+    t = graph_time(torch, go, iters, 4)
     nbytes = mat.n * mat.k * 2 + 2 * m * mat.k + 4 * m * mat.n
     del ws, w0
     torch.cuda.empty_cache()
@@ -535,33 +554,23 @@ def topk_rate(torch, q4, lib, mat, m, topk, iters):
 
 def gemm_multi_rate(torch, q4, lib, mats, m, iters):
     """The projections of one prefill batch: one q4_gemm_multi launch against one
-    q4_gemm launch per matrix (weights resident; activations with outliers)."""
+    q4_gemm launch per matrix (weights resident; activations with outliers),
+    each replayed from a HIP graph."""
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mats[0].k, outliers=True)).cuda()
     prods = [Product(torch, q4, mat, m, x, 1) for mat in mats]
     multi = MultiArgs(prods, 0)
-    sh = torch.cuda.current_stream().cuda_stream
 
-    def grouped():
+    def grouped(i, sh):
         st = lib.q4_gemm_multi(x.data_ptr(), m, multi.k, multi.count, multi.packed,
                                multi.scales, multi.y, multi.n, sh)
         if st != 0:
             raise RuntimeError("q4_gemm_multi failed with status %d" % st)
 
-    def separate():
+    def separate(i, sh):
         for p in prods:
             launch(lib, "q4_gemm", p.args(0), sh)
-
-    def timed(fn):
-        settle(torch, lambda i: fn())
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(iters):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / iters / 1e3
-    tg, ts = timed(grouped), timed(separate)
+    tg, ts = graph_time(torch, grouped, iters, 4), graph_time(torch, separate, iters, 4)
     flops = sum(p.flops for p in prods)
     del prods
     torch.cuda.empty_cache()
@@ -576,8 +585,9 @@ def gemm_case(torch, q4, lib, mat, m, outliers, iters):
     copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 9 // 16))) if m <= 8 else 1
     p = Product(torch, q4, mat, m, x, copies)
     fn = "q4_gemv" if m <= 8 else "q4_gemm"
-    sh = torch.cuda.current_stream().cuda_stream
-    t = time_launches(torch, lib, fn, p, iters, sh)
+    # launches replayed from a graph, so that the host's launch cost does not
+    # pace the short GEMMs (M = 16 takes ~10 us)
+    t = graph_rate(torch, lib, fn, p, iters, 4)
     out = {"matrix": mat.name, "m": m, "n": mat.n, "k": mat.k, "fn": fn, "us": round(t * 1e6, 3),
            "TFLOP_s": round(p.flops / t / 1e12, 2),
            "mfma_frac": round(p.flops / t / 1e12 / FP16_MFMA_PEAK_TFS, 4),
