@@ -91,6 +91,10 @@ struct Gemm {
 // depend only on its index inside its segment and on the launch's tile shape,
 // never on the other matrices of the launch.
 constexpr int kGemmMaxSegments = 8;
+// Workgroups per launch at most: the dispatch counts work-items in 32 bits, and
+// 2^20 workgroups of up to 1024 threads stay below that.  Larger tile counts
+// take several launches, each starting at its own first tile.
+constexpr int64_t kGemmMaxGrid = 1 << 20;
 struct GemmSegments {
     const uint8_t* packed[kGemmMaxSegments];
     const uint16_t* scales[kGemmMaxSegments];
@@ -107,7 +111,8 @@ static_assert(kGemmMaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MULT
 // AGPRs (four v_accvgpr_read per 16x16 block before the scale FMAs).
 template <int BM, int WN, int WK, int KG, int S>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
-    const uint16_t* __restrict__ x, GemmSegments seg, int M, int K, int G, SpliceConsts kc) {
+    const uint16_t* __restrict__ x, GemmSegments seg, int M, int K, int G, SpliceConsts kc,
+    int64_t tile_base) {
     using C = Gemm<BM, WN, WK, KG, S>;
     constexpr int MB = C::MB;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -117,14 +122,15 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const uint16_t* scales = seg.scales[0];
     float* y = seg.y[0];
     int64_t N = seg.n[0], tiles_n = seg.tiles_n[0], tile0 = seg.tile0[0];
+    const int64_t gt = tile_base + blockIdx.x;           // tile over all segments
 #pragma unroll
     for (int i = 1; i < kGemmMaxSegments; ++i) {
-        if (i < seg.count && (int64_t)blockIdx.x >= seg.tile0[i]) {
+        if (i < seg.count && gt >= seg.tile0[i]) {
             packed = seg.packed[i]; scales = seg.scales[i]; y = seg.y[i];
             N = seg.n[i]; tiles_n = seg.tiles_n[i]; tile0 = seg.tile0[i];
         }
     }
-    const int64_t tile = (int64_t)blockIdx.x - tile0;
+    const int64_t tile = gt - tile0;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar branches
@@ -360,15 +366,19 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
         seg.tile0[i] = tiles;
         tiles += seg.tiles_n[i] * ((m + BM - 1) / BM);
     }
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     static std::atomic<uint64_t> lds_done{0};           // devices already set up
     hipError_t e = allow_dynamic_lds(
         reinterpret_cast<const void*>(&gemm_kernel<BM, WN, WK, KG, S>), C::kLdsTotal, lds_done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
-                       dim3(C::kThreads), C::kLdsTotal, stream, x, seg, (int)m, (int)k,
-                       (int)(k / 32), kSpliceConsts);
-    return hipGetLastError();
+    for (int64_t base = 0; base < tiles; base += kGemmMaxGrid) {
+        const int64_t grid = tiles - base < kGemmMaxGrid ? tiles - base : kGemmMaxGrid;
+        hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S>), dim3((unsigned)grid),
+                           dim3(C::kThreads), C::kLdsTotal, stream, x, seg, (int)m, (int)k,
+                           (int)(k / 32), kSpliceConsts, base);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Tile shapes for m > 32, largest first, with the time one full round of

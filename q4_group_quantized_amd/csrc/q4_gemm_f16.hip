@@ -61,17 +61,21 @@ struct GemmF16 {
     static_assert(kLdsTotal <= 160 * 1024, "LDS of one CU");
 };
 
+// Workgroups per launch at most (the dispatch counts work-items in 32 bits);
+// larger tile counts take several launches, each from its own first tile.
+constexpr int64_t kGemmF16MaxGrid = 1 << 20;
+
 // At least two waves per SIMD: caps a wave at 256 registers, which keeps the
 // MFMA accumulators in VGPRs.
 template <int BM, int WN, int WK, int KG, int S>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_f16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ y,
-    int M, int64_t N, int K, int G, int64_t tiles_n) {
+    int M, int64_t N, int K, int G, int64_t tiles_n, int64_t tile_base) {
     using C = GemmF16<BM, WN, WK, KG, S>;
     constexpr int MB = C::MB;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = tile_base + blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar branches
     const int wn = wave % WN;
@@ -231,15 +235,19 @@ hipError_t launch_gemm_f16_t(const uint16_t* x, const uint16_t* w, float* y, int
     using C = GemmF16<BM, WN, WK, KG, S>;
     const int64_t tiles_n = (n + C::BN - 1) / C::BN;
     const int64_t tiles = tiles_n * ((m + BM - 1) / BM);
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     static std::atomic<uint64_t> lds_done{0};           // devices already set up
     hipError_t e = allow_dynamic_lds(
         reinterpret_cast<const void*>(&gemm_f16_kernel<BM, WN, WK, KG, S>), C::kLdsTotal, lds_done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, WN, WK, KG, S>), dim3((unsigned)tiles),
-                       dim3(C::kThreads), C::kLdsTotal, stream, x, w, y, (int)m, n, (int)k,
-                       (int)(k / 32), tiles_n);
-    return hipGetLastError();
+    for (int64_t base = 0; base < tiles; base += kGemmF16MaxGrid) {
+        const int64_t grid = tiles - base < kGemmF16MaxGrid ? tiles - base : kGemmF16MaxGrid;
+        hipLaunchKernelGGL((gemm_f16_kernel<BM, WN, WK, KG, S>), dim3((unsigned)grid),
+                           dim3(C::kThreads), C::kLdsTotal, stream, x, w, y, (int)m, n, (int)k,
+                           (int)(k / 32), tiles_n, base);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace

@@ -218,6 +218,49 @@ def test_scales_at_any_even_address(q4, orc, fn, m, k, offset):
     assert_within(y.astype(np.float64), y_ref, bound, "%s scales at +%d B" % (fn, 2 * offset))
 
 
+@pytest.fixture(scope="module")
+def max_rows_matrix():
+    """n = 2^31 - 1 rows (the largest n the contract allows) at k = 32: random
+    codes and scales in [0.001, 0.01] generated on the device (38 GB)."""
+    n, k = 2 ** 31 - 1, 32
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2 ** 31 - 1)
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=DEV).random_(0, 256, generator=g)
+    scales = torch.empty((n, 1), dtype=torch.float16, device=DEV).uniform_(0.001, 0.01,
+                                                                            generator=g)
+    torch.cuda.synchronize()
+    yield packed, scales
+    del packed, scales
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fn,m", [("q4_gemv", 1), ("q4_gemv", 2), ("q4_gemm", 9)])
+def test_maximum_rows(q4, orc, max_rows_matrix, fn, m):
+    """Row offsets past 2^32 bytes, and for q4_gemm 67 million tiles: more than
+    one launch's grid holds, so the tiles are spread over several launches.
+    Sampled rows -- the ends, launch-chunk and power-of-two boundaries, and
+    random ones -- are recomputed by the oracle."""
+    packed, scales = max_rows_matrix
+    n, k = packed.shape[0], packed.shape[1] * 2
+    rng = np.random.default_rng(m)
+    x = (rng.standard_normal((m, k)) * 2).astype(np.float16)
+    _log("%s m=%d n=%d k=%d" % (fn, m, n, k))
+    y = getattr(q4, fn)(gpu(x), packed, scales)
+    torch.cuda.synchronize()
+    rows = {0, 1, 31, 32, 2 ** 25 - 1, 2 ** 25, 2 ** 25 + 32, 2 ** 27 + 5, 2 ** 28 - 1, 2 ** 28,
+            2 ** 31 - 2 ** 20, n - 33, n - 2, n - 1}
+    rows |= set(int(r) for r in rng.integers(0, n, 64))
+    rows = np.array(sorted(rows))
+    idx = torch.from_numpy(rows).to(DEV)
+    rp = packed[idx].cpu().numpy()
+    rs = scales[idx].cpu().numpy().view(np.uint16)
+    y_rows = y[:, idx].cpu().numpy().astype(np.float64)
+    del y
+    torch.cuda.empty_cache()
+    y_ref, bound = orc.matmul(x, rp, rs)
+    assert_within(y_rows, y_ref, bound, "%s m=%d at n = 2^31 - 1" % (fn, m))
+
+
 @pytest.mark.parametrize("fn,m,k", [("q4_gemv", 1, 65536), ("q4_gemv", 8, 65536),
                                     ("q4_gemm", 40, 65536), ("q4_gemv", 1, 2 ** 20)])
 def test_long_k(q4, orc, fn, m, k):
