@@ -262,9 +262,12 @@ def test_maximum_rows(q4, orc, max_rows_matrix, fn, m):
 
 
 @pytest.mark.parametrize("fn,m,k", [("q4_gemv", 1, 65536), ("q4_gemv", 8, 65536),
-                                    ("q4_gemm", 40, 65536), ("q4_gemv", 1, 2 ** 20)])
+                                    ("q4_gemm", 40, 65536), ("q4_gemv", 1, 2 ** 20),
+                                    ("q4_gemv", 1, 2 ** 24), ("q4_gemv", 8, 2 ** 24),
+                                    ("q4_gemm", 9, 2 ** 24)])
 def test_long_k(q4, orc, fn, m, k):
-    """K beyond what one LDS pass of activations holds."""
+    """K beyond what one LDS pass of activations holds, up to the largest k
+    the contract allows (2^24)."""
     x, packed, scales, y_ref, bound = _case(orc, m, 3, k, seed=k + m)
     _log("%s m=%d n=3 k=%d" % (fn, m, k))
     y = product(q4, fn, x, packed, scales)
