@@ -86,7 +86,7 @@ def test_quantize_golden_groups(q4, orc):
 
 
 @pytest.mark.parametrize("n,k", [(1, 32), (3, 96), (17, 160), (64, 2560), (1000, 1024),
-                                 (33, 32 * 37), (5, 65536)])
+                                 (33, 32 * 37), (5, 65536), (2, 2 ** 24)])
 def test_quantize_bit_exact(q4, orc, n, k):
     rng = np.random.default_rng(n * 7919 + k)
     w = oracle_pins.spread_weights(rng, n, k)
@@ -598,6 +598,18 @@ def test_gemv_f16_product(q4, orc, m, n, k):
     y_ref, bound = orc.matmul_f16(x, w)
     assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound,
                   "q4_gemv_f16 m=%d n=%d k=%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("fn,m", [("q4_gemv_f16", 1), ("q4_gemv_f16", 8), ("q4_gemm_f16", 9)])
+def test_f16_longest_k(q4, orc, fn, m):
+    """fp16 weights at the largest k the contract allows (2^24), n = 3."""
+    n, k = 3, 2 ** 24
+    x, w = _f16_case(m, n, k, seed=m + 24)
+    _log("%s m=%d n=%d k=%d" % (fn, m, n, k))
+    y = getattr(q4, fn)(gpu(x), gpu(w))
+    torch.cuda.synchronize()
+    y_ref, bound = orc.matmul_f16(x, w)
+    assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound, "%s k = 2^24" % fn)
 
 
 def test_gemv_f16_exact_special_inputs(q4):
