@@ -12,7 +12,7 @@
 // the group's scale is applied in fp32 afterwards: acc += s[n, j] * P.  In the
 // 16x16 D layout a lane's four values share one column, hence one scale.
 //
-// Work split.  A workgroup (4 or 8 waves: one or two per SIMD) owns a
+// Work split.  A workgroup (4, 8 or 16 waves: one, two or four per SIMD) owns a
 // BM x (32*WN) tile of y (WN = 1, 2 or 4).  Its waves are WN column slices of 32 x WK slices of K: each wave covers
 // all BM rows and 32 columns over G/WK groups, so every code is unpacked by
 // exactly one wave and every activation is read from LDS by WN waves.  The
@@ -76,7 +76,7 @@ struct Gemm {
     static constexpr int kLdsTotal = kLdsBytes + kZeroBytes;
     static constexpr int kRedBytes = (WK - 1) * WN * MB * 8 * 64 * 4;
     static constexpr int kThreads = 64 * WN * WK;
-    static_assert(WN * WK == 4 || WN * WK == 8, "one or two waves per SIMD");
+    static_assert(WN * WK == 4 || WN * WK == 8 || WN * WK == 16, "one, two or four waves per SIMD");
     static_assert(WN <= 4 && H <= 2, "at most four column slices (128 columns)");
     static_assert((KG * MB) % WN == 0, "activation blocks split evenly");
     static_assert(S >= 2, "at least double buffering");
@@ -106,9 +106,10 @@ struct GemmSegments {
 };
 static_assert(kGemmMaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MULTI_MAX matrices");
 
-// At least two waves per SIMD: caps a wave at 256 registers, which also makes
-// the compiler keep MFMA results in VGPRs instead of routing them through
-// AGPRs (four v_accvgpr_read per 16x16 block before the scale FMAs).
+// At least two waves per SIMD: caps a wave at 256 registers (128 for the
+// 16-wave workgroups, which need four per SIMD), which also makes the compiler
+// keep MFMA results in VGPRs instead of routing them through AGPRs (four
+// v_accvgpr_read per 16x16 block before the scale FMAs).
 template <int BM, int WN, int WK, int KG, int S>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const uint16_t* __restrict__ x, GemmSegments seg, int M, int K, int G, SpliceConsts kc,
@@ -385,7 +386,7 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
 // them takes (k = 2560, n = 4096, one tile per CU; measured).
 constexpr TileChoice kTiles[] = {
     {128, 128, 35.f},      // gemm_kernel<128, 4, 2, 2, 2>
-    {64, 128, 23.f},       // gemm_kernel<64, 4, 2, 2, 2>
+    {64, 128, 22.f},       // gemm_kernel<64, 4, 4, 2, 2> (16 waves)
     {64, 64, 15.5f},       // gemm_kernel<64, 2, 4, 2, 2>
     {32, 64, 11.f},        // gemm_kernel<32, 2, 4, 2, 2>
 };
@@ -402,7 +403,7 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
     if (e != hipSuccess) return e;
     switch (choose_tile(kTiles, 4, m, count, n, device_info(dev).cu_count)) {
         case 0: return launch_gemm_t<128, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
-        case 1: return launch_gemm_t<64, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+        case 1: return launch_gemm_t<64, 4, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
         case 2: return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
         default: return launch_gemm_t<32, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
     }
