@@ -50,6 +50,11 @@ bytes per GEMV launch: each counter is scaled by the factor that maps the
 copy's reading onto the copy's known 256 MiB, and the result is stored with a
 hash of the kernel sources in profiles/gemv_lmhead_08b_traffic.txt, from where
 the roofline's `traffic` is read while the sources are unchanged.
+
+--gemm-probe runs five launches of the M = 512 prefill GEMM for `rocprofv3 --pmc`
+passes; --counter-summary COUNTERS.csv KEY prints the per-dispatch counter
+averages of the kernels whose name contains KEY (with MFMA busy time per SIMD
+and VALU instructions per MFMA when those counters are present).
 """
 from __future__ import annotations
 
@@ -198,6 +203,48 @@ def traffic_probe() -> int:
     torch.cuda.synchronize()
     log("traffic probe: 3 LM-head GEMVs and 3 copies of %d bytes done" % COPY_BYTES)
     return 0
+
+
+def gemm_probe() -> int:
+    """Five launches of the M = 512 prefill GEMM (4B projection, K = 2560,
+    N = 4096, outlier activations) for `rocprofv3 --pmc` passes."""
+    import torch
+    import q4_group_quantized_amd as q4
+    import q4_inputs as qi
+    lib = q4.load()
+    mat = qi.PREFILL_4B
+    x = torch.from_numpy(qi.activations(512, mat.k, outliers=True)).cuda()
+    p = Product(torch, q4, mat, 512, x, 1)
+    sh = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    for _ in range(5):
+        launch(lib, "q4_gemm", p.args(0), sh)
+    torch.cuda.synchronize()
+    log("gemm probe: 5 launches of q4_gemm m=512 n=%d k=%d done" % (mat.n, mat.k))
+    return 0
+
+
+def counter_summary(path: str, key: str) -> None:
+    """Per-dispatch averages of every counter in a rocprofv3 --pmc
+    counter_collection.csv for kernels whose name contains `key`, and the
+    MFMA busy fraction when its counters are present."""
+    sums, counts = {}, {}
+    for name, c, v in _counter_rows(path):
+        if key in name:
+            sums[c] = sums.get(c, 0.0) + v
+            counts[c] = counts.get(c, 0) + 1
+    avg = {c: sums[c] / counts[c] for c in sums}
+    for c in sorted(avg):
+        print("%-32s %18.1f   (%d dispatches)" % (c, avg[c], counts[c]))
+    simds = 256 * 4                          # MI355X: 256 CUs of 4 SIMDs
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        per = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+        print("MFMA busy cycles per SIMD: %.0f = %.2f us at 2.4 GHz" % (per, per / 2400.0))
+    if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
+        print("VALU instructions per MFMA instruction: %.2f" % (avg["SQ_INSTS_VALU"] /
+                                                               avg["SQ_INSTS_MFMA"]))
+    if "SQ_INSTS_VALU_MFMA_MOPS_F16" in avg:
+        print("MFMA f16 flops per dispatch: %.4g" % (avg["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512))
 
 
 # --------------------------------------------------------------------------
@@ -666,12 +713,17 @@ def main() -> int:
     ap.add_argument("--rocprof-summary", metavar="TRACE_CSV_OR_DB")
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--gemm-probe", action="store_true")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("COUNTER_CSV", "KERNEL_KEY"))
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
         return 0
     if args.traffic_record:
         traffic_record(*args.traffic_record)
+        return 0
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -687,6 +739,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.gemm_probe:
+        return gemm_probe()
     if args.traffic_probe:
         return traffic_probe()
     lib = q4.load()
