@@ -52,15 +52,17 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
     return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-template <int BM, int WN, int WK, int KG, int S>
+template <int BM, int WN, int WK, int KG, int S, int NB = 2>
 struct Gemm {
     static constexpr int MB = BM / 16;                     // 16-row blocks per wave
-    static constexpr int BN = 32 * WN;
+    static constexpr int BN = 16 * NB * WN;                        // NB 16-column blocks per wave
     static constexpr int H = (BN + 63) / 64;                         // 64-column code blocks
-    // 32-column tiles load the codes and scales of two groups per instruction
-    // (lanes 0-31 and 32-63); 64-column blocks take one group per instruction
-    static constexpr bool kPair = BN == 32;
-    static constexpr int kItems = kPair ? (KG + 1) / 2 : KG * H;    // code blocks per stage
+    // 16- and 32-column tiles load the codes and scales of 64 / BN groups per
+    // instruction (lanes BN*j .. BN*j + BN-1 take group j of the block); 64-column
+    // blocks take one group per instruction
+    static constexpr bool kPair = BN < 64;
+    static constexpr int kGPI = kPair ? 64 / BN : 1;                 // groups per code block
+    static constexpr int kItems = kPair ? (KG + kGPI - 1) / kGPI : KG * H;   // per stage
     static constexpr int kCodeOff = KG * MB * kBlockBytes;           // within a stage
     static constexpr int kScaleOff = kCodeOff + kItems * kBlockBytes;
     static constexpr int kStageBytes = kScaleOff + kItems * 256;     // per K slice
@@ -74,7 +76,7 @@ struct Gemm {
     // zeros that the operand reads of out-of-range groups are pointed at
     static constexpr int kZeroBytes = MB * kBlockBytes;
     static constexpr int kLdsTotal = kLdsBytes + kZeroBytes;
-    static constexpr int kRedBytes = (WK - 1) * WN * MB * 8 * 64 * 4;
+    static constexpr int kRedBytes = (WK - 1) * WN * MB * NB * 4 * 64 * 4;
     static constexpr int kThreads = 64 * WN * WK;
     static_assert(WN * WK == 4 || WN * WK == 8 || WN * WK == 16, "one, two or four waves per SIMD");
     static_assert(WN <= 4 && H <= 2, "at most four column slices (128 columns)");
@@ -110,11 +112,11 @@ static_assert(kGemmMaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MULT
 // 16-wave workgroups, which need four per SIMD), which also makes the compiler
 // keep MFMA results in VGPRs instead of routing them through AGPRs (four
 // v_accvgpr_read per 16x16 block before the scale FMAs).
-template <int BM, int WN, int WK, int KG, int S>
+template <int BM, int WN, int WK, int KG, int S, int NB>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const uint16_t* __restrict__ x, GemmSegments seg, int M, int K, int G, SpliceConsts kc,
     int64_t tile_base) {
-    using C = Gemm<BM, WN, WK, KG, S>;
+    using C = Gemm<BM, WN, WK, KG, S, NB>;
     constexpr int MB = C::MB;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -177,10 +179,10 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     const uint16_t* scale_row0 = scales + ld_col0 * G;
     const uint16_t* scale_row1 = scales + ld_col1 * G;
     // paired layout: lane = column (lane % 32) of group 2i + lane / 32
-    const int64_t pr_col = min<int64_t>(nt0 + (lane & 31), N - 1);
+    const int64_t pr_col = min<int64_t>(nt0 + lane % C::BN, N - 1);
     const uint8_t* code_rowp = packed + pr_col * (K / 2);
     const uint16_t* scale_rowp = scales + pr_col * G;
-    const int pr_g = lane >> 5;
+    const int pr_g = lane / C::BN;
     // operand-side lane mapping
     const int col = lane & 15, kq = lane >> 4;
 
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
         if constexpr (C::kPair) {
 #pragma unroll
             for (int it = 0; it < C::kItems; ++it) {
-                const int g = min(gs + 2 * it + pr_g, G - 1);
+                const int g = min(gs + C::kGPI * it + pr_g, G - 1);
                 __builtin_amdgcn_global_load_lds(code_rowp + 16 * g,
                                                  (lds_void_t*)(sb + C::kCodeOff + it * kBlockBytes),
                                                  16, 0, 0);
@@ -224,11 +226,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
         }
     };
 
-    float4_t acc[MB][2];
+    float4_t acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
     const uint32_t mask = kc.mask;
     const uint32_t magic = to_vgpr(kc.magic);
@@ -241,41 +243,41 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     // MFMAs and scale FMAs run, the next group's reads are in flight.
     struct Ops {
         half8_t a[MB];
-        uint32_t code[2];
-        _Float16 sc[2];
+        uint32_t code[NB];
+        _Float16 sc[NB];
     };
     auto read_ops = [&](Ops& o, const unsigned char* sb, int gl, bool valid) {
         const unsigned char* ab = valid ? sb + gl * MB * kBlockBytes : zero;
-        const int item = C::kPair ? gl >> 1 : gl * C::H;            // first code block of group gl
-        const int e0 = C::kPair ? 32 * (gl & 1) : 0;                   // its first entry there
+        const int item = C::kPair ? gl / C::kGPI : gl * C::H;       // first code block of group gl
+        const int e0 = C::kPair ? C::BN * (gl % C::kGPI) : 0;         // its first entry there
         const unsigned char* scb = valid ? sb + C::kScaleOff + item * 256 : zero;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
             o.a[mb] = *reinterpret_cast<const half8_t*>(ab + mb * kBlockBytes + 64 * col + 16 * kq);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int c = 32 * wn + 16 * nb + col;
+        for (int nb = 0; nb < NB; ++nb) {
+            const int c = 16 * NB * wn + 16 * nb + col;
             o.code[nb] = *reinterpret_cast<const uint32_t*>(
                 sb + C::kCodeOff + item * kBlockBytes + 16 * (e0 + c) + 4 * kq);
             o.sc[nb] = *reinterpret_cast<const _Float16*>(scb + 4 * (e0 + c));
         }
     };
     auto compute = [&](const Ops& o) {
-        half8_t bh[2];
+        half8_t bh[NB];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bh[nb] = unpack8_natural(o.code[nb], mask, magic, sel);
+        for (int nb = 0; nb < NB; ++nb) bh[nb] = unpack8_natural(o.code[nb], mask, magic, sel);
         // all MFMAs of the group first, so their latencies overlap, then the
         // scale FMAs
-        float4_t p[MB][2];
+        float4_t p[MB][NB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
                 const float4_t zero = {0.f, 0.f, 0.f, 0.f};
                 p[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a[mb], bh[nb], zero, 0, 0, 0);
             }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
             const float s = (float)o.sc[nb];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -324,10 +326,10 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    red[((((kp - 1) * WN + wn) * MB + mb) * 8 + nb * 4 + v) * 64 + lane] =
+                    red[((((kp - 1) * WN + wn) * MB + mb) * NB * 4 + nb * 4 + v) * 64 + lane] =
                         acc[mb][nb][v];
     }
     __syncthreads();
@@ -335,14 +337,14 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int64_t n = nt0 + 32 * wn + 16 * nb + col;
+            for (int nb = 0; nb < NB; ++nb) {
+                const int64_t n = nt0 + 16 * NB * wn + 16 * nb + col;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     float t = acc[mb][nb][v];
 #pragma unroll
                     for (int q = 1; q < WK; ++q)
-                        t += red[((((q - 1) * WN + wn) * MB + mb) * 8 + nb * 4 + v) * 64 + lane];
+                        t += red[((((q - 1) * WN + wn) * MB + mb) * NB * 4 + nb * 4 + v) * 64 + lane];
                     const int64_t m = m0 + 16 * mb + 4 * kq + v;
                     if (m < M && n < N) y[m * N + n] = t;
                 }
@@ -350,11 +352,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
     }
 }
 
-template <int BM, int WN, int WK, int KG, int S>
+template <int BM, int WN, int WK, int KG, int S, int NB = 2>
 hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* packed,
                          const uint16_t* const* scales, float* const* y, const int64_t* n,
                          int64_t m, int64_t k, hipStream_t stream) {
-    using C = Gemm<BM, WN, WK, KG, S>;
+    using C = Gemm<BM, WN, WK, KG, S, NB>;
     GemmSegments seg = {};
     seg.count = count;
     int64_t tiles = 0;
@@ -369,11 +371,11 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
     }
     static std::atomic<uint64_t> lds_done{0};           // devices already set up
     hipError_t e = allow_dynamic_lds(
-        reinterpret_cast<const void*>(&gemm_kernel<BM, WN, WK, KG, S>), C::kLdsTotal, lds_done);
+        reinterpret_cast<const void*>(&gemm_kernel<BM, WN, WK, KG, S, NB>), C::kLdsTotal, lds_done);
     if (e != hipSuccess) return e;
     for (int64_t base = 0; base < tiles; base += kGemmMaxGrid) {
         const int64_t grid = tiles - base < kGemmMaxGrid ? tiles - base : kGemmMaxGrid;
-        hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((gemm_kernel<BM, WN, WK, KG, S, NB>), dim3((unsigned)grid),
                            dim3(C::kThreads), C::kLdsTotal, stream, x, seg, (int)m, (int)k,
                            (int)(k / 32), kSpliceConsts, base);
         e = hipGetLastError();
@@ -394,8 +396,8 @@ constexpr TileChoice kTiles[] = {
 hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* const* packed,
                                 const uint16_t* const* scales, float* const* y,
                                 const int64_t* n, int64_t m, int64_t k, hipStream_t stream) {
-    if (m <= 16)
-        return launch_gemm_t<16, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
+    if (m <= 16)      // 16 x 16 tiles: the weight traffic of a small batch spread over every CU
+        return launch_gemm_t<16, 1, 4, 4, 4, 1>(x, count, packed, scales, y, n, m, k, stream);
     if (m <= 32)
         return launch_gemm_t<32, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
     int dev = 0;
