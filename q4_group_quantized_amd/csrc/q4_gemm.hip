@@ -13,8 +13,10 @@
 // 16x16 D layout a lane's four values share one column, hence one scale.
 //
 // Work split.  A workgroup (4, 8 or 16 waves: one, two or four per SIMD) owns a
-// BM x (32*WN) tile of y (WN = 1, 2 or 4).  Its waves are WN column slices of 32 x WK slices of K: each wave covers
-// all BM rows and 32 columns over G/WK groups, so every code is unpacked by
+// BM x (16*NB*WN) tile of y (WN = 1, 2 or 4 column slices of NB = 1 or 2
+// 16-column blocks).  Its waves are WN column slices x WK slices of K: each
+// wave covers all BM rows and 16*NB columns over G/WK groups, so every code is
+// unpacked by
 // exactly one wave and every activation is read from LDS by WN waves.  The
 // WK partial tiles are added in LDS at the end in a fixed order
 // (deterministic).  The tile shape is chosen per launch from m and the number
