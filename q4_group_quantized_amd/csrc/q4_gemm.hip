@@ -400,8 +400,8 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
                                 const int64_t* n, int64_t m, int64_t k, hipStream_t stream) {
     if (m <= 16)      // 16 x 16 tiles: the weight traffic of a small batch spread over every CU
         return launch_gemm_t<16, 1, 4, 4, 4, 1>(x, count, packed, scales, y, n, m, k, stream);
-    if (m <= 32)
-        return launch_gemm_t<32, 1, 4, 2, 4>(x, count, packed, scales, y, n, m, k, stream);
+    if (m <= 32)      // 32 x 16 tiles (measured 10.5 -> 8.0 us at m = 32, n = 4096, k = 2560)
+        return launch_gemm_t<32, 1, 4, 4, 3, 1>(x, count, packed, scales, y, n, m, k, stream);
     int dev = 0;
     const hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
