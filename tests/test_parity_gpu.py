@@ -153,7 +153,8 @@ def test_single_token_streaming(q4, orc, n, k):
     assert_within(y, y_ref, bound, "q4_gemv m=1 n=%d k=%d" % (n, k))
 
 
-@pytest.mark.parametrize("m", [9, 15, 16, 17, 31, 64, 100, 128, 129, 300, 1024, 1100])
+@pytest.mark.parametrize("m", [9, 15, 16, 17, 24, 31, 32, 33, 64, 100, 128, 129, 300, 1024,
+                               1100])
 @pytest.mark.parametrize("n,k", [(17, 96), (64, 256), (130, 2560), (200, 160), (70, 1056)])
 def test_prefill_product(q4, orc, m, n, k):
     x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m * 31 + n * 7 + k)
@@ -191,7 +192,8 @@ def test_blockdiag_lds_limits(q4, orc, m, n, k):
 
 
 SCALE_OFFSET_CASES = [("q4_gemv", 1, 1024), ("q4_gemv", 2, 1024), ("q4_gemv", 5, 544),
-                      ("q4_gemv", 8, 7936), ("q4_gemv", 3, 16384), ("q4_gemm", 40, 1024)]
+                      ("q4_gemv", 8, 7936), ("q4_gemv", 3, 16384), ("q4_gemm", 40, 1024),
+                      ("q4_gemm", 16, 1056), ("q4_gemm", 32, 1056)]
 
 
 @pytest.mark.parametrize("fn,m,k", SCALE_OFFSET_CASES,
@@ -262,7 +264,8 @@ def test_maximum_rows(q4, orc, max_rows_matrix, fn, m):
 
 
 @pytest.mark.parametrize("fn,m,k", [("q4_gemv", 1, 65536), ("q4_gemv", 8, 65536),
-                                    ("q4_gemm", 40, 65536), ("q4_gemv", 1, 2 ** 20),
+                                    ("q4_gemm", 40, 65536), ("q4_gemm", 16, 65536),
+                                    ("q4_gemm", 32, 65536), ("q4_gemv", 1, 2 ** 20),
                                     ("q4_gemv", 1, 2 ** 24), ("q4_gemv", 8, 2 ** 24),
                                     ("q4_gemm", 9, 2 ** 24)])
 def test_long_k(q4, orc, fn, m, k):
@@ -379,6 +382,9 @@ def test_gemv_multi_binding_errors(q4):
 GEMM_MULTI_SETS = [
     (9, 256, (15, 100)),
     (40, 1056, (33, 7, 64)),
+    (16, 1056, (33, 7, 64)),                               # 16 x 16 tiles
+    (24, 2560, (130, 5, 257)),                             # 32 x 16 tiles
+    (32, 1056, (17, 100, 3, 64)),
     (128, 2560, (130, 5, 257, 64)),
     (300, 96, (17, 200, 3, 1, 70, 33, 9, 129)),            # eight matrices
     (512, 1024, (100, 61)),
@@ -485,6 +491,34 @@ def select_topk(y_row, topk):
     return order[:topk]
 
 
+def assert_valid_topk(sel, y_ref, bound, what):
+    """`sel` (rows, best first) is a correct top-k of the oracle's products
+    given that every logit may sit anywhere within its tolerance: for every
+    selected row s and every row u ranked after it (later in the list, or not
+    selected), y_ref[s] + tol[s] >= y_ref[u] - tol[u].  Several selections can
+    pass when logits are closer than their tolerances; any of them is a
+    correct greedy / top-k candidate set."""
+    n = len(y_ref)
+    sel = np.asarray(sel, dtype=np.int64)
+    assert len(set(sel.tolist())) == len(sel), "%s: repeated rows %s" % (what, sel)
+    assert np.all((sel >= 0) & (sel < n)), "%s: rows out of range" % what
+    tol = oracle.tolerance(bound)
+    hi = y_ref + tol
+    lo = y_ref - tol
+    rest = np.ones(n, dtype=bool)
+    rest[sel] = False
+    if rest.any():
+        worst_sel = hi[sel].min()
+        best_rest = lo[rest].max()
+        assert worst_sel >= best_rest, (
+            "%s: selected row %d (ref %.9g + tol) ranks below unselected row %d (ref %.9g - tol)"
+            % (what, sel[np.argmin(hi[sel])], y_ref[sel[np.argmin(hi[sel])]],
+               np.flatnonzero(rest)[np.argmax(lo[rest])], best_rest))
+    # the order inside the list: each entry can be at least every later one
+    later_lo = np.maximum.accumulate(lo[sel][::-1])[::-1]
+    assert np.all(hi[sel][:-1] >= later_lo[1:]), "%s: list order contradicts the oracle" % what
+
+
 TOPK_CASES = [(1, 1, 256, 1), (1, 5, 1024, 5), (1, 33, 96, 20), (1, 1000, 1024, 20),
               (1, 4099, 2560, 32), (1, 70001, 1024, 20), (1, 3000, 8192, 7),
               (2, 1000, 256, 20), (5, 4099, 1024, 1), (8, 70001, 2560, 20), (8, 64, 96, 32)]
@@ -493,7 +527,8 @@ TOPK_CASES = [(1, 1, 256, 1), (1, 5, 1024, 5), (1, 33, 96, 20), (1, 1000, 1024, 
 @pytest.mark.parametrize("m,n,k,topk", TOPK_CASES, ids=["m%d-n%d-k%d-top%d" % c for c in TOPK_CASES])
 def test_gemv_topk_selects_from_the_gemv_logits(q4, orc, m, n, k, topk):
     """The selection is exact on the kernel's own fp32 logits (those of q4_gemv, bit for
-    bit); the selected logits are also within tolerance of the oracle's."""
+    bit), every logit is within tolerance of the oracle's, and the selection is a valid
+    top-k of the oracle's products (assert_valid_topk)."""
     x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m * 3 + n + k + topk)
     xg, pg, sg = gpu(x), gpu(packed), gpu(scales.view(np.float16))
     _log("q4_gemv_topk m=%d n=%d k=%d topk=%d" % (m, n, k, topk))
@@ -502,11 +537,14 @@ def test_gemv_topk_selects_from_the_gemv_logits(q4, orc, m, n, k, topk):
     torch.cuda.synchronize()
     lg = logits.cpu().numpy()
     vals, rws = values.cpu().numpy(), rows.cpu().numpy()
+    # every logit of the kernel within tolerance of the oracle's
+    assert_within(lg.astype(np.float64), y_ref, bound, "q4_gemv logits")
     for i in range(m):
         want = select_topk(lg[i], topk)
         assert np.array_equal(rws[i], want), "token %d rows %s != %s" % (i, rws[i][:8], want[:8])
         assert np.array_equal(vals[i].view(np.uint32), lg[i][want].view(np.uint32))
         assert_within(vals[i].astype(np.float64), y_ref[i][want], bound[i][want], "topk values")
+        assert_valid_topk(rws[i], y_ref[i], bound[i], "token %d" % i)
 
 
 @pytest.mark.parametrize("m,n", [(1, 300), (1, 5000), (3, 5000)])
@@ -552,22 +590,35 @@ def test_gemv_topk_deterministic_and_errors(q4, orc):
     assert q4.q4_gemv_topk_workspace_size(1, 5000, 1024) > 0
 
 
-@pytest.mark.parametrize("key,m,topk", [("decode_08b", 1, 20), ("decode_4b", 8, 20)])
-def test_gemv_topk_lm_head_full_size(q4, key, m, topk):
-    """The full LM head: the fused selection equals the selection on q4_gemv's logits."""
+@pytest.mark.parametrize("key,m,topk", [("decode_08b", 1, 20), ("decode_08b", 1, 1),
+                                         ("decode_4b", 1, 20), ("decode_4b", 8, 20)])
+def test_gemv_topk_lm_head_full_size(q4, orc, key, m, topk):
+    """The full 248,320-row LM head: the fused selection equals the selection on
+    q4_gemv's logits, every logit is within tolerance of the oracle's product
+    (computed for all rows from the oracle's own quantization of the same
+    generated weights), and the selection is a valid top-k of the oracle's
+    products."""
     mat = qi.WORKLOADS[key].cases[-1][0]
     _log("topk %s m=%d: generating" % (mat.name, m))
     w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)
     packed, scales = q4.q4_quantize(gpu(w))
+    rp, rs = orc.quantize(w)
     del w
-    xg = gpu(qi.activations(m, mat.k))
+    x = qi.activations(m, mat.k)
+    xg = gpu(x)
     values, rows = q4.q4_gemv_topk(xg, packed, scales, topk)
     lg = q4.q4_gemv(xg, packed, scales).cpu().numpy()
     torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), rp), "codes differ from the oracle's"
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), rs), "scales differ"
+    _log("topk %s m=%d: oracle product over all rows" % (mat.name, m))
+    y_ref, bound = orc.matmul(x, rp, rs)
+    assert_within(lg.astype(np.float64), y_ref, bound, "%s logits" % mat.name)
     for i in range(m):
         want = select_topk(lg[i], topk)
         assert np.array_equal(rows.cpu().numpy()[i], want)
         assert np.array_equal(values.cpu().numpy()[i].view(np.uint32), lg[i][want].view(np.uint32))
+        assert_valid_topk(rows.cpu().numpy()[i], y_ref[i], bound[i], "%s token %d" % (mat.name, i))
 
 
 # --------------------------------------------------------------------------
@@ -762,7 +813,7 @@ def test_gemm_f16_prefill_full_size(q4, orc, m):
 
 
 # --------------------------------------------------------------------------
-# the five workload configurations at full size, compared on sampled rows
+# the five workload configurations at full size, compared in full
 # --------------------------------------------------------------------------
 
 def _sample_rows(n, rng, count=384):
@@ -777,6 +828,9 @@ CASES = [(wl.key, i) for wl in qi.WORKLOADS.values() for i in range(len(wl.cases
 
 @pytest.mark.parametrize("key,idx", CASES, ids=["%s-%d" % c for c in CASES])
 def test_workload_full_size(q4, orc, key, idx):
+    """Every code, scale and output of the configuration against the oracle,
+    which quantizes the same generated weights itself and computes the whole
+    product in fp64."""
     wl = qi.WORKLOADS[key]
     mat, m = wl.cases[idx]
     fn = "q4_gemv" if m <= 8 else "q4_gemm"
@@ -789,14 +843,14 @@ def test_workload_full_size(q4, orc, key, idx):
     _log("%s: %s" % (mat.name, fn))
     y = getattr(q4, fn)(gpu(x), packed, scales)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(mat.tensor_id)
-    rows = _sample_rows(mat.n, rng)
-    rows_t = torch.from_numpy(rows).to(DEV)
-    gp = packed.index_select(0, rows_t).cpu().numpy()
-    gs = scales.index_select(0, rows_t).cpu().numpy().view(np.uint16)
-    gy = y.index_select(1, rows_t).cpu().numpy().astype(np.float64)
-    # the oracle quantizes the same generated rows itself
-    rp, rs = orc.quantize(w[rows])
-    assert np.array_equal(gs, rs) and np.array_equal(gp, rp), "quantize mismatch"
+    gp = packed.cpu().numpy()
+    gs = scales.cpu().numpy().view(np.uint16)
+    gy = y.cpu().numpy()
+    del packed, scales, y
+    _log("%s: oracle quantize + product over all rows" % mat.name)
+    rp, rs = orc.quantize(w)
+    del w
+    assert np.array_equal(gs, rs), "scales differ from the oracle's"
+    assert np.array_equal(gp, rp), "codes differ from the oracle's"
     y_ref, bound = orc.matmul(x, rp, rs)
-    assert_within(gy, y_ref, bound, "%s %s" % (key, mat.name))
+    assert_within(gy.astype(np.float64), y_ref, bound, "%s %s" % (key, mat.name))
