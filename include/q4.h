@@ -58,10 +58,11 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 6
+#define Q4_ABI_VERSION 7
 #define Q4_GROUP 32
 #define Q4_MULTI_MAX 8
 #define Q4_TOPK_MAX 32
+#define Q4_NOALLOC_SCRATCH_BYTES (16u << 20)   /* q4_gemv_topk_noalloc's buffer */
 
 typedef enum {
     Q4_OK = 0,
@@ -70,7 +71,8 @@ typedef enum {
     Q4_ERR_ALIGN = 3,   /* a pointer breaks the alignment rule                */
     Q4_ERR_LAUNCH = 4,  /* the HIP runtime refused or failed the launch       */
     Q4_ERR_DEVICE = 5,  /* no usable gfx950 device is current                 */
-    Q4_ERR_WORKSPACE = 6 /* workspace NULL, smaller than required or not 256-B aligned */
+    Q4_ERR_WORKSPACE = 6, /* workspace NULL, smaller than required or not 256-B aligned */
+    Q4_ERR_TOO_LARGE = 7  /* q4_gemv_topk_noalloc: scratch need above Q4_NOALLOC_SCRATCH_BYTES */
 } q4_status;
 
 /* Version of this interface; equals Q4_ABI_VERSION of the built library. */
@@ -192,6 +194,27 @@ q4_status q4_gemv_topk(const uint16_t* x, const uint8_t* packed,
                        const uint16_t* scales, int64_t m, int64_t n, int64_t k,
                        int32_t topk, float* values, int32_t* rows,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * q4_gemv_topk_noalloc -- q4_gemv_topk for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same kernels and
+ * bit-identical results as q4_gemv_topk; the scratch comes from a buffer of
+ * Q4_NOALLOC_SCRATCH_BYTES (16 MiB) that the library keeps on every device it
+ * runs on until the process ends.  The call allocates and frees nothing; its
+ * first call on a device looks that device's buffer up (hipGetSymbolAddress).
+ *   Arguments as q4_gemv_topk, without workspace and workspace_bytes.
+ * Errors: as q4_gemv_topk; a problem whose workspace
+ * (q4_gemv_topk_workspace_size) exceeds Q4_NOALLOC_SCRATCH_BYTES ->
+ * Q4_ERR_TOO_LARGE (the 248,320-row LM head fits at every m <= 8), and
+ * nothing is launched.
+ * All calls on one device share its buffer: calls that overlap in time on
+ * one device (several streams or host threads) race and must be serialised
+ * by the caller.  No part of the buffer needs clearing between calls.
+ */
+q4_status q4_gemv_topk_noalloc(const uint16_t* x, const uint8_t* packed,
+                               const uint16_t* scales, int64_t m, int64_t n, int64_t k,
+                               int32_t topk, float* values, int32_t* rows, void* stream);
 
 /*
  * q4_gemm -- prefill product, same arguments and semantics as q4_gemv, for

@@ -15,6 +15,7 @@ Functions keep the C names:
   q4_gemm_f16(x, w)                    -> y fp32 [m,n]     (fp16 weights, any m)
   q4_gemv_topk(x, packed, scales, topk) -> (values fp32 [m,topk], rows int32 [m,topk])
   q4_gemv_topk_workspace_size(m, n, k) -> bytes of device workspace q4_gemv_topk needs
+  q4_gemv_topk_noalloc(x, packed, scales, topk) -> as q4_gemv_topk, scratch held by the library
   q4_status_str(code), q4_abi_version()
 Outputs may be passed in (``out=``) to avoid allocation.
 """
@@ -29,9 +30,10 @@ LIB_PATH = os.path.join(_PKG, "libq4.so")
 
 EXPORTED = ("q4_abi_version", "q4_status_str", "q4_quantize", "q4_gemv", "q4_gemm",
             "q4_gemv_multi", "q4_gemm_multi", "q4_gemv_f16", "q4_gemm_f16", "q4_gemv_topk",
-            "q4_gemv_topk_workspace_size")
+            "q4_gemv_topk_workspace_size", "q4_gemv_topk_noalloc")
 (Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_LAUNCH, Q4_ERR_DEVICE,
- Q4_ERR_WORKSPACE) = range(7)
+ Q4_ERR_WORKSPACE, Q4_ERR_TOO_LARGE) = range(8)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 TOPK_MAX = 32
 GROUP = 32
 MULTI_MAX = 8
@@ -78,6 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q4_gemv_topk.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int32, p, p, p,
                                  ctypes.c_size_t, p]
     lib.q4_gemv_topk.restype = ctypes.c_int
+    lib.q4_gemv_topk_noalloc.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int32, p, p, p]
+    lib.q4_gemv_topk_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -283,4 +287,34 @@ def q4_gemv_topk(x, packed, scales, topk, workspace=None, out=None, stream=None)
                                  int(topk), values.data_ptr(), rows.data_ptr(), ws_ptr + pad,
                                  ws_bytes, _stream(stream, x.device))
     _check("q4_gemv_topk", st)
+    return values, rows
+
+
+def q4_gemv_topk_noalloc(x, packed, scales, topk, out=None, stream=None):
+    """q4_gemv_topk without a workspace: the library's own scratch buffer
+    (NOALLOC_SCRATCH_BYTES per device) serves the call, so the C call
+    allocates nothing.  Calls that overlap in time on one device race on that
+    buffer.  `out` may pass the (values fp32 [m, topk], rows int32 [m, topk])
+    tensors; otherwise they are allocated here with torch."""
+    import torch
+    _require(x, torch.float16, "x")
+    _require(packed, torch.uint8, "packed")
+    _require(scales, torch.float16, "scales")
+    m, k = x.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 2 != k or tuple(scales.shape) != (n, k // GROUP):
+        raise ValueError("shapes disagree: x %s packed %s scales %s"
+                         % (tuple(x.shape), tuple(packed.shape), tuple(scales.shape)))
+    if out is None:
+        values = torch.empty((m, topk), dtype=torch.float32, device=x.device)
+        rows = torch.empty((m, topk), dtype=torch.int32, device=x.device)
+    else:
+        values, rows = out
+        _require(values, torch.float32, "values")
+        _require(rows, torch.int32, "rows")
+    with torch.cuda.device(x.device):
+        st = load().q4_gemv_topk_noalloc(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), m,
+                                         n, k, int(topk), values.data_ptr(), rows.data_ptr(),
+                                         _stream(stream, x.device))
+    _check("q4_gemv_topk_noalloc", st)
     return values, rows

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libq4.so")
 
-SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemv_f16.hip", "q4_gemm.hip", "q4_gemm_f16.hip", "q4_topk.hip"]
+SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemv_f16.hip", "q4_gemm.hip", "q4_gemm_f16.hip", "q4_topk.hip",
+           "q4_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -106,6 +106,7 @@ const char* q4_status_str(q4_status status) {
         case Q4_ERR_LAUNCH: return "kernel launch failed";
         case Q4_ERR_DEVICE: return "current device is not a usable gfx950";
         case Q4_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case Q4_ERR_TOO_LARGE: return "problem needs more scratch than the built-in buffer holds";
     }
     return "unknown status";
 }
