@@ -1,54 +1,57 @@
 #!/usr/bin/env python3
 """Throughput of the gfx950 Q4 group-quantized GEMV/GEMM path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-Prints ONE JSON line.  The workload is the 0.8B-shaped decode set at M = 1
-(hidden 1024: DeltaNet q/k/v 3 x 2048 rows, attention q 2048, k 512, v 512,
-LM head 248,320 rows), weights ~ N(0, 0.02^2) quantized on the GPU, x ~ N(0,1)
-in fp16.  One step is one decode pass over the seven matrices, launched as the
-model would group them by shared input: one q4_gemv_multi for the DeltaNet
-q/k/v projections, one for the attention q/k/v projections, and the LM head,
-replayed from a HIP graph (detail also times seven separate q4_gemv launches
-and one launch over all seven).  The step rotates through enough copies of
-the quantized weights (>= 1 GiB) that no step finds its weights in the 256 MB
-Infinity Cache: the figure is HBM-bound throughput, not cache bandwidth.
+Prints ONE JSON line.  The headline workload is the 4B-shaped decode set at
+M = 1 (hidden 2560: DeltaNet q/k 2048 rows each, v 4096, attention q 4096,
+k 1024, v 1024, LM head 248,320 rows), weights ~ N(0, 0.02^2) quantized on the
+GPU, x ~ N(0,1) in fp16.  One step is one decode pass over the seven
+matrices, launched as the model groups them by shared input: one
+q4_gemv_multi for the DeltaNet q/k/v projections, one for the attention
+q/k/v projections, and the LM head, replayed from a HIP graph.  The step
+rotates through enough copies of the quantized weights (>= 1 GiB) that no
+step finds its weights in the 256 MB Infinity Cache: the figure is HBM-bound
+throughput, not cache bandwidth.
 
-value    = algorithmic bytes of one step / step time (GB/s); algorithmic bytes
-           of one product = n*k/2 (codes) + n*k/16 (fp16 scales) + 2*m*k (x)
-           + 4*m*n (y)
-roofline = the dominant kernel (the LM-head GEMV): its algorithmic bytes per
-           launch / its average launch duration (HIP events on the launching
-           stream around a batch of back-to-back launches over the rotated
-           copies, after ~20 ms of untimed launches of the same kernel: every
-           timed batch here starts past the clock ramp of sustained traffic),
-           against the 8 TB/s HBM3E peak
-detail   = the other halves of the hot path measured in the same run: the 4B
-           LM head (k = 2560), the 0.8B LM head with its top-20 epilogue
-           (q4_gemv_topk, against q4_gemv + torch.topk), the 0.8B LM head in
-           the fp16 weight format (q4_gemv_f16, 2 bytes per weight), the
-           M = 512 prefill GEMM, the six 4B projections of one M = 512 batch
-           in one q4_gemm_multi launch (against six q4_gemm launches) (TFLOP/s against the
-           2.5 PFLOP/s dense fp16 MFMA peak) and the quantizer (GB/s); --all
-           adds the 4B decode set, the M = 8 verify LM head and the
-           M = 16/128/2048 prefill GEMMs.  The GEMMs, the verify head and the
-           fp16-weight products are timed as back-to-back launches replayed
-           from a HIP graph (after ~20 ms of replays), so host launch cost
-           does not pace them
-cpu_baseline = the CPU oracle (plain C, fp64 product) on a bounded sample of
-           the same decode set, GB/s over the same algorithmic bytes
+value     = algorithmic bytes of one step / step time (GB/s); algorithmic bytes
+            of one product = n*k/2 (codes) + n*k/16 (fp16 scales) + 2*m*k (x)
+            + 4*m*n (y)
+roofline  = the dominant kernel (the 4B LM-head GEMV, m = 1, k = 2560): its
+            algorithmic bytes per launch / its average launch duration (HIP
+            events on the launching stream around a batch of back-to-back
+            launches over the rotated copies, after ~20 ms of untimed launches
+            of the same kernel), against the 8 TB/s HBM3E peak
+gemm_m512 = the metric's second half: the M = 512 prefill GEMM (K = 2560,
+            N = 4096, activations with outlier channels), TFLOP/s against the
+            2.5 PFLOP/s dense fp16 MFMA peak
+detail    = every other configuration, each timed in the same run: the
+            0.8B decode set and its LM head, the single 1024 x 1024 GEMV, the
+            M = 16 / 128 prefill GEMMs, the M = 8 verify LM head and the
+            M = 2048 GEMM (wide-scale weights), the launch floor (an empty
+            kernel), the top-k epilogue, the fp16-weight products, the grouped
+            prefill GEMM and the quantizer.  GEMMs, the verify head and the
+            fp16-weight products are timed as back-to-back launches replayed
+            from a HIP graph (after ~20 ms of replays), so host launch cost
+            does not pace them
+cpu_baseline = the CPU oracle (plain C, fp64 product) on bounded row samples
+            of the same configurations, GB/s over the same algorithmic bytes;
+            the CPU model, the threads used, quantizer and product per
+            configuration and a single-threaded 0.8B LM-head run
 
---rocprof-summary TRACE.csv groups a rocprofv3 kernel trace by kernel and
-grid size (the LM head and the projections run the same kernel at different
-grid sizes) and prints average durations.
+--rocprof-summary TRACE [--tail N] groups a rocprofv3 kernel trace by kernel
+and grid size (the LM head and the projections run the same kernel at
+different grid sizes) and prints average durations, and with --tail N also
+the average of each group's last N launches (the roofline batch is the last
+batch of the LM-head kernel at its grid size).
 
---traffic-probe runs three launches of the 0.8B LM-head GEMV and three of a
+--traffic-probe runs three launches of the 4B LM-head GEMV and three of a
 plain elementwise copy of known size (torch.neg over 256 MiB of fp32), for two
 `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` passes;
 --traffic-record FETCH.csv WRITE.csv turns their counter files into the HBM
 bytes per GEMV launch: each counter is scaled by the factor that maps the
 copy's reading onto the copy's known 256 MiB, and the result is stored with a
-hash of the kernel sources in profiles/gemv_lmhead_08b_traffic.txt, from where
+hash of the kernel sources in profiles/gemv_lmhead_4b_traffic.txt, from where
 the roofline's `traffic` is read while the sources are unchanged.
 
 --gemm-probe runs five launches of the M = 512 prefill GEMM for `rocprofv3 --pmc`
@@ -72,7 +75,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFS = 2500.0    # MI355X dense fp16 MFMA
 ROTATE_BYTES = 1 << 30         # rotate through >= 1 GiB of weight copies
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lmhead_08b_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lmhead_4b_traffic.txt")
 COPY_BYTES = 256 << 20         # read (and written) by the traffic-calibration copy
 KERNEL_SOURCES = ["q4_group_quantized_amd/csrc/q4_gemv.hip",
                   "q4_group_quantized_amd/csrc/q4_device.hpp"]
@@ -94,27 +97,39 @@ def kernel_source_hash() -> str:
 # rocprofv3 trace summary
 # --------------------------------------------------------------------------
 
-def rocprof_summary(path: str) -> None:
+def rocprof_summary(path: str, tail: int = 0) -> None:
     """Average kernel durations by (kernel, grid size) from a rocprofv3 kernel
-    trace: either a *_kernel_trace.csv or a rocpd *_results.db."""
+    trace: either a *_kernel_trace.csv or a rocpd *_results.db.  With `tail`,
+    also the average of each group's last `tail` launches (in start order)."""
     groups = {}
     if path.endswith(".db"):
         import sqlite3
         con = sqlite3.connect(path)
-        for name, grid, dur in con.execute("select name, grid_x, end - start from kernels"):
-            groups.setdefault((name, str(grid)), []).append(int(dur))
+        for name, grid, start, end in con.execute(
+                "select name, grid_x, start, end from kernels"):
+            groups.setdefault((name, str(grid)), []).append((int(start), int(end) - int(start)))
     else:
         import csv
         with open(path) as fh:
             for row in csv.DictReader(fh):
                 name = row.get("Kernel_Name", "?")
                 grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "?"
-                dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
-                groups.setdefault((name, grid), []).append(dur)
-    print("%-10s %-8s %-12s %-12s %s" % ("grid_x", "calls", "avg_ns", "min_ns", "kernel"))
-    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+                start = int(row["Start_Timestamp"])
+                groups.setdefault((name, grid), []).append(
+                    (start, int(row["End_Timestamp"]) - start))
+    head = "%-10s %-8s %-12s %-12s" % ("grid_x", "calls", "avg_ns", "min_ns")
+    if tail:
+        head += " %-14s" % ("last%d_avg_ns" % tail)
+    print(head + " kernel")
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+        d.sort()
+        durs = [x[1] for x in d]
         short = name if len(name) < 100 else name[:97] + "..."
-        print("%-10s %-8d %-12.0f %-12d %s" % (grid, len(d), sum(d) / len(d), min(d), short))
+        line = "%-10s %-8d %-12.0f %-12d" % (grid, len(durs), sum(durs) / len(durs), min(durs))
+        if tail:
+            last = durs[-tail:]
+            line += " %-14.0f" % (sum(last) / len(last))
+        print(line + " " + short)
 
 
 def _counter_rows(path: str):
@@ -154,11 +169,11 @@ def traffic_record(fetch_csv: str, write_csv: str) -> None:
     c_write = _counter_avg(write_csv, "WRITE_SIZE", "neg")
     f_fetch = COPY_BYTES / (c_fetch * 1024.0)
     f_write = COPY_BYTES / (c_write * 1024.0)
-    mat = qi.DECODE_08B[-1]
+    mat = qi.DECODE_4B[-1]
     algo = qi.workload_bytes(1, mat.n, mat.k)
     traffic = g_fetch * 1024.0 * f_fetch + g_write * 1024.0 * f_write
     lines = [
-        "# HBM traffic of one q4_gemv launch on the 0.8B LM head (m=1, n=%d, k=%d)" % (mat.n, mat.k),
+        "# HBM traffic of one q4_gemv launch on the 4B LM head (m=1, n=%d, k=%d)" % (mat.n, mat.k),
         "# Commands (REPO = the repository root, OUT = any output directory; one counter per run):",
         "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $OUT/pmcf "
         "-o f --output-format csv -- python3 $REPO/bench.py --traffic-probe",
@@ -190,7 +205,7 @@ def traffic_probe() -> int:
     import q4_group_quantized_amd as q4
     import q4_inputs as qi
     lib = q4.load()
-    mat = qi.DECODE_08B[-1]
+    mat = qi.DECODE_4B[-1]
     x = torch.from_numpy(qi.activations(1, mat.k)).cuda()
     p = Product(torch, q4, mat, 1, x, 1)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -201,7 +216,7 @@ def traffic_probe() -> int:
         launch(lib, "q4_gemv", p.args(0), sh)
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    log("traffic probe: 3 LM-head GEMVs and 3 copies of %d bytes done" % COPY_BYTES)
+    log("traffic probe: 3 4B LM-head GEMVs and 3 copies of %d bytes done" % COPY_BYTES)
     return 0
 
 
@@ -251,15 +266,28 @@ def counter_summary(path: str, key: str) -> None:
 # GPU helpers
 # --------------------------------------------------------------------------
 
+_HOST_WEIGHTS = {}
+
+
+def host_weights(mat):
+    """The generated fp32 weights of `mat` (numpy), kept for later products on
+    the same matrix: drawing the 248,320-row heads takes seconds each."""
+    import q4_inputs as qi
+    w = _HOST_WEIGHTS.get(mat)
+    if w is None:
+        w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id, wide_groups=mat.wide_groups)
+        if mat.n * mat.k >= 1 << 20:
+            _HOST_WEIGHTS[mat] = w
+    return w
+
+
 class Product:
     """One quantized matrix resident in HBM, with rotation copies and an output."""
 
     def __init__(self, torch, q4, mat, m, x, copies, outliers=False):
         import q4_inputs as qi
         self.mat, self.m = mat, m
-        w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id, wide_groups=mat.wide_groups)
-        wg = torch.from_numpy(w).cuda()
-        del w
+        wg = torch.from_numpy(host_weights(mat)).cuda()
         packed, scales = q4.q4_quantize(wg)
         del wg
         self.copies = [(packed, scales)] + [(packed.clone(), scales.clone())
@@ -413,6 +441,9 @@ def decode_set(torch, q4, lib, workload, warmup, steps, side_steps):
                 if not torch.equal(p.y, e):
                     raise RuntimeError("%s graph of copy %d differs from the eager run"
                                        % (mode, c))
+        # past the clock ramp of sustained traffic (SETTLE_S of replays), then
+        # the requested warmup steps
+        settle(torch, lambda i: graphs[i % copies].replay())
         for i in range(warmup):
             graphs[i % copies].replay()
         torch.cuda.synchronize()
@@ -494,13 +525,17 @@ def graph_time(torch, go, launches, replays):
 
 
 def small_gemv_latency(torch, q4, lib):
-    """The latency-bound end: the single 1024 x 1024 GEMV and a one-row,
-    one-group GEMV (the cost of any launch through the library), both from a
-    graph of back-to-back launches."""
+    """The latency-bound end, each from a graph of back-to-back launches: an
+    empty kernel (a one-element fill, the cheapest launch there is), a
+    one-row, one-group GEMV (the cost of any launch through the library) and
+    the single 1024 x 1024 GEMV."""
     import q4_inputs as qi
     out = {}
+    one = torch.empty(1, dtype=torch.float32, device="cuda")
+    t = graph_time(torch, lambda i, sh: one.fill_(float(i)), 64, 20)
+    out["empty_kernel"] = {"kernel": "torch one-element fill", "us": round(t * 1e6, 3)}
     for key, mat in (("single_1024", qi.WORKLOADS["single"].cases[0][0]),
-                     ("launch_floor", qi.Matrix("floor", 1, 32, 0))):
+                     ("one_group_gemv", qi.Matrix("floor", 1, 32, 0))):
         x = torch.from_numpy(qi.activations(1, mat.k)).cuda()
         p = Product(torch, q4, mat, 1, x, 64)
         t = graph_rate(torch, lib, "q4_gemv", p, 64, 20)
@@ -532,7 +567,7 @@ def f16_gemv_rate(torch, q4, lib, mat, m, iters, fn="q4_gemv_f16", outliers=Fals
     copies, replayed from a HIP graph."""
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
-    w0 = torch.from_numpy(qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)).cuda().half()
+    w0 = torch.from_numpy(host_weights(mat)).cuda().half()
     copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 2)))
     ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     y = torch.empty((m, mat.n), dtype=torch.float32, device=x.device)
@@ -647,7 +682,7 @@ def gemm_case(torch, q4, lib, mat, m, outliers, iters):
 
 def quantize_rate(torch, q4, mat, iters):
     import q4_inputs as qi
-    w = torch.from_numpy(qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id)).cuda()
+    w = torch.from_numpy(host_weights(mat)).cuda()
     packed = torch.empty((mat.n, mat.k // 2), dtype=torch.uint8, device=w.device)
     scales = torch.empty((mat.n, mat.k // 32), dtype=torch.float16, device=w.device)
     settle(torch, lambda i: q4.q4_quantize(w, out=(packed, scales)))
@@ -670,35 +705,90 @@ def quantize_rate(torch, q4, mat, iters):
 # CPU baseline: the oracle on a bounded sample of the decode set
 # --------------------------------------------------------------------------
 
-def cpu_baseline(workload, budget_s=10.0):
-    """Oracle product over the whole decode set, repeated for ~budget_s."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_time(fn, budget_s, max_runs=50):
+    """Median wall time of fn() over repeated runs for about budget_s."""
+    times = []
+    start = time.perf_counter()
+    while not times or (time.perf_counter() - start < budget_s and len(times) < max_runs):
+        t = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t)
+    times.sort()
+    return times[len(times) // 2], len(times)
+
+
+# rows of each matrix the CPU baseline quantizes and multiplies: at most
+# CPU_SAMPLE_ROWS, and at most CPU_SAMPLE_MACS multiply-adds per product run
+# (at least 64 rows; the whole matrix when it has fewer)
+CPU_SAMPLE_ROWS = 16384
+CPU_SAMPLE_MACS = 300_000_000
+
+
+def cpu_baseline():
+    """The oracle as it stands, on the host cores of this machine: quantizer
+    and product timed separately on a row sample of every configuration
+    (median of repeated runs), GB/s over the sample's algorithmic bytes (the
+    same formulas as the GPU figures).  `value` is the product over the 4B
+    decode set's samples at M = 1, the headline workload.  Also one
+    single-threaded product run on the 0.8B LM head sample."""
+    import numpy as np
     import oracle
     import q4_inputs as qi
     o = oracle.get()
-    mats = [mat for mat, _ in workload.cases]
-    x = qi.activations(1, mats[0].k, outliers=workload.outliers)
-    quantized = []
-    t0 = time.perf_counter()
-    for mat in mats:
-        w = qi.weights(mat.n, mat.k, tensor_id=mat.tensor_id, wide_groups=mat.wide_groups)
-        tq = time.perf_counter()
-        quantized.append(o.quantize(w))
-        t0 += time.perf_counter() - tq     # generation time is not oracle work
-    set_bytes = sum(qi.workload_bytes(1, mat.n, mat.k) for mat in mats)
-    times = []
-    start = time.perf_counter()
-    while not times or (time.perf_counter() - start < budget_s and len(times) < 1000):
-        t = time.perf_counter()
-        for p, s in quantized:
-            o.matmul(x, p, s)
-        times.append(time.perf_counter() - t)
-    times.sort()
-    med = times[len(times) // 2]
-    return {"value": round(set_bytes / med / 1e9, 3), "unit": "GB/s", "cores": o.threads(),
-            "kind": "oracle",
-            "sample": ("whole 0.8B decode set at M=1 (7 matrices, %.1f MB algorithmic), oracle "
-                       "q4o_matmul in fp64, median of %d passes (%.1f s)"
-                       % (set_bytes / 1e6, len(times), sum(times)))}
+    threads = o.threads()
+    per_config = {}
+    headline_bytes, headline_s = 0, 0.0
+    single_08b = None
+    for key, wl in qi.WORKLOADS.items():
+        rows_out = []
+        for mat, m in wl.cases:
+            rows = min(mat.n, CPU_SAMPLE_ROWS, max(64, CPU_SAMPLE_MACS // (m * mat.k)))
+            w = qi.weight_rows(mat.n, mat.k, 0, rows, tensor_id=mat.tensor_id,
+                               wide_groups=mat.wide_groups)
+            x = qi.activations(m, mat.k, outliers=wl.outliers)
+            tq, _ = _median_time(lambda: o.quantize(w), 0.3, 5)
+            packed, scales = o.quantize(w)
+            tp, runs = _median_time(lambda: o.matmul(x, packed, scales), 0.5, 9)
+            qbytes = rows * mat.k * 4 + rows * mat.k // 2 + rows * (mat.k // 32) * 2
+            pbytes = qi.workload_bytes(m, rows, mat.k)
+            rows_out.append({"matrix": mat.name, "m": m, "rows": rows, "k": mat.k,
+                             "quantize_GB_s": round(qbytes / tq / 1e9, 3),
+                             "product_GB_s": round(pbytes / tp / 1e9, 3),
+                             "product_GFLOP_s": round(2.0 * m * rows * mat.k / tp / 1e9, 3)})
+            if key == "decode_4b":
+                headline_bytes += pbytes
+                headline_s += tp
+            if key == "decode_08b" and mat.name.endswith("lm_head"):
+                o.set_threads(1)
+                try:
+                    t1, _ = _median_time(lambda: o.matmul(x, packed, scales), 1.0, 3)
+                finally:
+                    o.set_threads(threads)
+                single_08b = {"matrix": mat.name, "m": m, "rows": rows, "k": mat.k,
+                              "threads": 1, "product_GB_s": round(pbytes / t1 / 1e9, 3)}
+            del w, packed, scales
+        per_config[key] = rows_out
+    return {"value": round(headline_bytes / headline_s / 1e9, 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": ("oracle product (fp64) at M=1 over the first %d rows of each of the 4B "
+                       "decode set's 7 matrices (whole projections, LM-head sample), %.1f MB "
+                       "algorithmic, median of repeated runs; per_config times the quantizer "
+                       "and the product on the first min(n, %d, %d / (m k)) rows of every "
+                       "configuration" % (CPU_SAMPLE_ROWS, headline_bytes / 1e6,
+                                          CPU_SAMPLE_ROWS, CPU_SAMPLE_MACS)),
+            "per_config": per_config, "single_thread_lm_head_08b": single_08b}
 
 
 # --------------------------------------------------------------------------
@@ -706,18 +796,19 @@ def cpu_baseline(workload, budget_s=10.0):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--all", action="store_true", help="also time the other configurations")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rocprof-summary", metavar="TRACE_CSV_OR_DB")
+    ap.add_argument("--tail", type=int, default=0,
+                    help="with --rocprof-summary: also average each group's last N launches")
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--gemm-probe", action="store_true")
     ap.add_argument("--counter-summary", nargs=2, metavar=("COUNTER_CSV", "KERNEL_KEY"))
     args = ap.parse_args()
     if args.rocprof_summary:
-        rocprof_summary(args.rocprof_summary)
+        rocprof_summary(args.rocprof_summary, args.tail)
         return 0
     if args.traffic_record:
         traffic_record(*args.traffic_record)
@@ -745,18 +836,25 @@ def main() -> int:
         return traffic_probe()
     lib = q4.load()
     torch.cuda.set_device(0)
-
-    wl = qi.WORKLOADS["decode_08b"]
+    sh = torch.cuda.current_stream().cuda_stream
     side = max(50, args.steps // 4)
-    log("decode set 0.8B: building")
+
+    def modes(d):
+        return {m: {"us_per_step": round(t * 1e6, 2),
+                    "GB_s": round(d["set_bytes"] / t / 1e9, 1)} for m, t in d["modes_s"].items()}
+
+    # ---- headline: one decode pass over the 4B-shaped set -----------------
+    wl = qi.WORKLOADS["decode_4b"]
+    log("decode set 4B: building")
     ds = decode_set(torch, q4, lib, wl, args.warmup, args.steps, side)
     value = ds["set_bytes"] / ds["step_s"] / 1e9
 
-    # dominant kernel: the LM-head GEMV, back-to-back launches over the
+    # dominant kernel: the 4B LM-head GEMV, back-to-back launches over the
     # rotated copies, HIP events on the launching stream around the batch
+    # (the last batch of this kernel at this grid size in the run)
     lm = ds["prods"][-1]
-    sh = torch.cuda.current_stream().cuda_stream
-    lm_t = time_launches(torch, lib, "q4_gemv", lm, max(200, 8 * ds["copies"]), sh)
+    lm_iters = max(200, 8 * ds["copies"])
+    lm_t = time_launches(torch, lib, "q4_gemv", lm, lm_iters, sh)
     achieved = lm.bytes / lm_t / 1e9
     traffic = None
     tr = read_traffic_file()
@@ -764,57 +862,66 @@ def main() -> int:
         traffic = int(tr["bytes_per_launch"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "q4_gemv LM head m=1 n=248320 k=1024",
-                "bytes_per_launch": lm.bytes, "avg_launch_us": round(lm_t * 1e6, 3)}
+                "kernel": "q4_gemv 4B LM head m=1 n=%d k=%d" % (lm.mat.n, lm.mat.k),
+                "bytes_per_launch": lm.bytes, "avg_launch_us": round(lm_t * 1e6, 3),
+                "batch_launches": lm_iters}
+    detail = {"decode_4b_modes": modes(ds), "decode_4b_per_matrix": ds["per_matrix"],
+              "rotation_copies_4b": ds["copies"]}
     del ds["prods"], lm
     torch.cuda.empty_cache()
 
-    def modes(d):
-        return {m: {"us_per_step": round(t * 1e6, 2),
-                    "GB_s": round(d["set_bytes"] / t / 1e9, 1)} for m, t in d["modes_s"].items()}
-
-    detail = {"decode_08b_modes": modes(ds), "decode_08b_per_matrix": ds["per_matrix"],
-              "rotation_copies": ds["copies"]}
-    log("LM head 4B")
-    detail["lm_head_4b"] = lm_head_rate(torch, q4, lib, qi.DECODE_4B[-1], 100)
-    log("LM head 0.8B with top-20 epilogue")
-    detail["lm_head_topk20_08b"] = topk_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 20, 100)
-    log("F16 GEMV LM head 0.8B")
-    detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
+    # ---- the metric's second half: the M = 512 prefill GEMM --------------
     log("prefill GEMM M=512")
+    g512 = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
+    gemm_m512 = {"us": g512["us"], "TFLOP_s": g512["TFLOP_s"], "mfma_frac": g512["mfma_frac"],
+                 "peak_TFLOP_s": FP16_MFMA_PEAK_TFS,
+                 "shape": "M=512 K=2560 N=4096, x with 1% outlier channels x20"}
+
+    # ---- every other configuration --------------------------------------
+    log("decode set 0.8B")
+    d08 = decode_set(torch, q4, lib, qi.WORKLOADS["decode_08b"], args.warmup, side, side)
+    detail["decode_08b_modes"] = modes(d08)
+    detail["decode_08b_per_matrix"] = d08["per_matrix"]
+    lm08 = d08["prods"][-1]
+    t08 = time_launches(torch, lib, "q4_gemv", lm08, max(200, 8 * d08["copies"]), sh)
+    detail["lm_head_08b"] = {"matrix": lm08.mat.name, "n": lm08.mat.n, "k": lm08.mat.k,
+                             "us": round(t08 * 1e6, 3),
+                             "GB_s": round(lm08.bytes / t08 / 1e9, 1),
+                             "hbm_frac": round(lm08.bytes / t08 / 1e9 / HBM_PEAK_GBS, 4)}
+    del d08["prods"], lm08
+    torch.cuda.empty_cache()
+    log("latency floor and the single 1024 x 1024 GEMV")
     detail["small_gemv_latency"] = small_gemv_latency(torch, q4, lib)
-    detail["gemm_m512"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
-    detail["f16_gemm_m512"] = f16_gemv_rate(torch, q4, lib, qi.PREFILL_4B, 512, 100,
-                                            fn="q4_gemm_f16", outliers=True)
+    for m in (16, 128):
+        log("prefill GEMM M=%d" % m)
+        detail["gemm_m%d" % m] = gemm_case(torch, q4, lib, qi.PREFILL_4B, m, True, 100)
+    detail["gemm_m512"] = g512
+    log("prefill GEMM M=2048 (wide-scale weights)")
+    detail["gemm_m2048"] = gemm_case(torch, q4, lib, qi.PREFILL_4B_WIDE, 2048, False, 30)
+    log("verify LM head M=8 (wide-scale weights)")
+    detail["verify_m8_lm_head"] = gemm_case(torch, q4, lib, qi.LM_HEAD_4B_WIDE, 8, False, 50)
+    log("top-k epilogues")
+    detail["lm_head_topk20_08b"] = topk_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 20, 100)
+    detail["lm_head_argmax_4b_m8"] = topk_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 1, 30)
     log("grouped prefill GEMM: 4B projections, M=512")
     detail["gemm_multi_4b_proj_m512"] = gemm_multi_rate(torch, q4, lib, list(qi.DECODE_4B[:-1]),
                                                         512, 50)
-    log("quantize 0.8B LM head")
+    log("fp16-weight products")
+    detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
+    detail["f16_gemv_lm_head_4b_m8"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 30)
+    detail["f16_gemm_m512"] = f16_gemv_rate(torch, q4, lib, qi.PREFILL_4B, 512, 100,
+                                            fn="q4_gemm_f16", outliers=True)
+    detail["f16_gemm_m2048"] = f16_gemv_rate(torch, q4, lib, qi.PREFILL_4B_WIDE, 2048, 30,
+                                             fn="q4_gemm_f16")
+    log("quantizer: LM heads")
     detail["quantize_lm_head_08b"] = quantize_rate(torch, q4, qi.DECODE_08B[-1], 10)
-    if args.all:
-        log("decode set 4B")
-        d4 = decode_set(torch, q4, lib, qi.WORKLOADS["decode_4b"], args.warmup, side, side)
-        detail["decode_4b_modes"] = modes(d4)
-        detail["decode_4b_per_matrix"] = d4["per_matrix"]
-        del d4
-        torch.cuda.empty_cache()
-        for m in (16, 128, 2048):
-            log("prefill GEMM M=%d" % m)
-            mat = qi.PREFILL_4B if m != 2048 else qi.PREFILL_4B_WIDE
-            detail["gemm_m%d" % m] = gemm_case(torch, q4, lib, mat, m, m != 2048, 50)
-        log("verify LM head M=8")
-        detail["verify_m8_lm_head"] = gemm_case(torch, q4, lib, qi.LM_HEAD_4B_WIDE, 8, False, 50)
-        log("verify LM head M=8 with argmax epilogue")
-        detail["lm_head_argmax_4b_m8"] = topk_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 1, 30)
-        log("F16 GEMV LM head 4B, M=8")
-        detail["f16_gemv_lm_head_4b_m8"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 30)
-        detail["f16_gemm_m2048"] = f16_gemv_rate(torch, q4, lib, qi.PREFILL_4B_WIDE, 2048, 30,
-                                                 fn="q4_gemm_f16")
+    detail["quantize_lm_head_4b"] = quantize_rate(torch, q4, qi.DECODE_4B[-1], 5)
+    _HOST_WEIGHTS.clear()
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(wl)
+        cpu = cpu_baseline()
 
     out = {
         "metric": "Q4 GEMV HBM GB/s (% of peak) at M=1; Q4 GEMM TFLOP/s (% MFMA peak) M=512",
@@ -829,12 +936,14 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16xq4->f32",
         "data": "synthetic",
-        "config": {"workload": "0.8B-shaped Q4 decode set, M=1, K=1024 (7 matrices incl. "
+        "config": {"workload": "4B-shaped Q4 decode set, M=1, K=2560 (7 matrices incl. "
                                "248320-row LM head) as 3 launches: DeltaNet q/k/v and "
                                "attention q/k/v each one q4_gemv_multi, LM head; weights "
                                "rotated over %d copies" % ds["copies"],
-                   "m": 1, "k": 1024, "n": [mat.n for mat, _ in wl.cases],
+                   "m": 1, "k": 2560, "n": [mat.n for mat, _ in wl.cases],
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "gemm_m512": gemm_m512,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": detail,

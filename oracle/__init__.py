@@ -60,10 +60,16 @@ class Oracle:
         lib.q4o_matmul.restype = ctypes.c_int
         lib.q4o_threads.argtypes = []
         lib.q4o_threads.restype = ctypes.c_int
+        lib.q4o_set_threads.argtypes = [ctypes.c_int]
+        lib.q4o_set_threads.restype = None
         self.lib = lib
 
     def threads(self) -> int:
         return int(self.lib.q4o_threads())
+
+    def set_threads(self, threads: int) -> None:
+        """Thread count of later calls (timing only: results never depend on it)."""
+        self.lib.q4o_set_threads(int(threads))
 
     # -- scalar conversions -------------------------------------------------
     def f32_to_f16_bits(self, f: float) -> int:

@@ -259,3 +259,13 @@ int q4o_threads(void) {
     return 1;
 #endif
 }
+
+/* Sets the thread count of later parallel loops (for timing; no effect on
+ * any result, which never depends on the split over threads). */
+void q4o_set_threads(int threads) {
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+}

@@ -38,4 +38,7 @@ int q4o_matmul_f16(const uint16_t* x, const uint16_t* w, int64_t m, int64_t n,
 /* Threads used by the parallel loops. */
 int q4o_threads(void);
 
+/* Thread count of later parallel loops (results do not depend on it). */
+void q4o_set_threads(int threads);
+
 #endif
