@@ -386,13 +386,484 @@ hipError_t launch_gemm_t(const uint16_t* x, int count, const uint8_t* const* pac
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// m > 32: 32 x 32 output blocks (v_mfma_f32_32x32x16_f16)
+//
+// Per 32-element group and 32 x 32 block: two MFMAs (K = 16 each) into a
+// fresh P, then acc += s * P, where a lane's 16 values of the 32 x 32 D
+// layout share one column (lane % 32) and hence one scale.  Per MAC this
+// issues half the MFMA instructions of 16 x 16 blocks; the sixteen fp32 scale
+// FMAs per block and group are the same count either way.
+//
+// Work split.  A workgroup of WN x WK waves owns a BM x BN tile of y (BM =
+// 32 MB rows, BN = 32 NB WN columns).  Wave (wn, wk) computes all BM rows of
+// columns [32 NB wn, 32 NB (wn + 1)) over the groups wk, wk + WK, ... of
+// every stage, so a code is unpacked once per workgroup and shared by the MB
+// row blocks.  The WK partial tiles are added in LDS in a fixed order.
+//
+// Data movement.  A stage holds KG consecutive groups of the tile: every
+// operand goes global -> LDS with direct loads, each wave instruction
+// reading whole rows of the stage (activations: 64/(4 KG) rows x 64 KG
+// bytes; codes: 64/KG columns x 16 KG bytes; scales: 64 of them, 2 bytes
+// each into 4-byte slots).  LDS layouts are XOR-swizzled so that the
+// operand reads of a wave touch distinct banks: activation chunk c (16 B)
+// of tile row r sits at position c ^ (r & 7) of the row, code group gl of
+// column j at position gl ^ ((j >> 1) & (KG - 1)).  The loads choose their
+// global addresses to fill those positions, so the loop reads LDS at fixed
+// per-lane offsets and issues no address arithmetic per operand.
+// K mapping inside a group: lane (i, g) (i = lane % 32, g = lane / 32) feeds
+// the MFMA h (h = 0, 1) with the 8 elements of chunk 2g + h, for the
+// activation row i and for the code column i alike.
+// ---------------------------------------------------------------------------
+typedef float float16v_t __attribute__((ext_vector_type(16)));
+// Per-lane load offsets are kept in a vector type: with a plain local array
+// in the address of a direct-to-LDS load the host compiler drops the
+// kernel's launch stub.
+typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
+
+template <int MB, int NB, int WN, int WK, int KG, int S, bool SV>
+struct G32 {
+    static constexpr int BM = 32 * MB;
+    static constexpr int BN = 32 * NB * WN;
+    static constexpr int W = WN * WK;
+    static constexpr int kThreads = 64 * W;
+    static constexpr int GPW = KG / WK;                  // groups per wave and stage
+    static constexpr int kRowBytes = KG * 64;            // activations of one row
+    static constexpr int kColBytes = KG * 16;            // codes of one column
+    static constexpr int kABytes = BM * kRowBytes;
+    static constexpr int kCBytes = BN * kColBytes;
+    // scales: SV (4-byte loads of two groups): [column][KG groups] fp16;
+    // else one 2-byte load per (group, column) into 4-byte slots,
+    // [group][column]
+    static constexpr int kSBytes = SV ? BN * KG * 2 : KG * BN * 4;
+    static constexpr int kStage = kABytes + kCBytes + kSBytes;
+    static constexpr int NA = kABytes / 1024;            // load instructions per stage
+    static constexpr int NC = kCBytes / 1024;
+    static constexpr int NS = SV ? BN * KG / 128 : KG * BN / 64;
+    static constexpr int NAW = NA / W, NCW = NC / W, NSW = NS / W;
+    static constexpr int kLoadsPerWave = NAW + NCW + NSW;
+    // partial tiles of K phases 1..WK-1, then the final tile row-major
+    static constexpr int kRedBytes = (WK > 1 ? WK - 1 : 1) * BM * BN * 4;
+    static constexpr int kLds = S * kStage > kRedBytes ? S * kStage : kRedBytes;
+    static constexpr int CPR = 4 * KG;                   // 16-byte chunks per activation row
+    static constexpr int RPI = 64 / CPR;                 // rows per load instruction
+    static constexpr int CPI = 64 / KG;                  // code columns per load instruction
+    static_assert(KG % WK == 0, "whole groups per wave");
+    static_assert(KG == 2 || KG == 4 || KG == 8 || KG == 16, "power-of-two stage");
+    static_assert(!SV || KG % 2 == 0, "4-byte scale loads hold two groups");
+    static_assert(NA % W == 0 && NC % W == 0 && NS % W == 0, "equal loads per wave");
+    static_assert(W == 4 || W == 8 || W == 16, "one, two or four waves per SIMD");
+    static_assert(NAW <= 16 && NCW <= 16 && NSW <= 16, "load offsets fit one u32x16_t");
+    static_assert(S >= 2, "at least double buffering");
+    static_assert(kLds <= 160 * 1024, "LDS of one CU");
+};
+
+template <int MB, int NB, int WN, int WK, int KG, int S, bool SV, bool TAIL>
+__global__ __launch_bounds__(64 * WN * WK, 1) void gemm32_kernel(
+    const uint16_t* __restrict__ x, GemmSegments seg, int M, int K, int G, SpliceConsts kc,
+    int64_t tile_base, int vec_store) {
+    using C = G32<MB, NB, WN, WK, KG, S, SV>;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const uint8_t* packed = seg.packed[0];
+    const uint16_t* scales = seg.scales[0];
+    float* y = seg.y[0];
+    int64_t N = seg.n[0], tiles_n = seg.tiles_n[0], tile0 = seg.tile0[0];
+    const int64_t gt = tile_base + blockIdx.x;
+#pragma unroll
+    for (int i = 1; i < kGemmMaxSegments; ++i) {
+        if (i < seg.count && gt >= seg.tile0[i]) {
+            packed = seg.packed[i]; scales = seg.scales[i]; y = seg.y[i];
+            N = seg.n[i]; tiles_n = seg.tiles_n[i]; tile0 = seg.tile0[i];
+        }
+    }
+    const int64_t tile = gt - tile0;
+    const int64_t n0 = (tile % tiles_n) * C::BN;
+    const int64_t m0 = (tile / tiles_n) * C::BM;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % WN, wk = wave / WN;
+    const int li = lane & 31, lg = lane >> 5;
+    const int nstages = (G + KG - 1) / KG;
+
+    // ---- per-lane load offsets (bytes from the stage's uniform bases) ----
+    u32x16_t offA = {}, offC = {}, offS = {};
+    int ldsA[C::NAW], ldsC[C::NCW], ldsS[C::NSW];
+    int grpA[C::NAW], grpC[C::NCW], grpS[C::NSW];   // group of the stage each lane loads
+#pragma unroll
+    for (int t = 0; t < C::NAW; ++t) {
+        const int q = wave * C::NAW + t;
+        const int r = q * C::RPI + lane / C::CPR;
+        const int c = (lane % C::CPR) ^ (r & 7);
+        const int64_t row = min<int64_t>(m0 + r, M - 1) - m0;
+        grpA[t] = c >> 2;
+        offA[t] = (uint32_t)(row * K * 2) + (uint32_t)(c * 16);
+        ldsA[t] = q * 1024;
+    }
+#pragma unroll
+    for (int t = 0; t < C::NCW; ++t) {
+        const int q = wave * C::NCW + t;
+        const int j = q * C::CPI + lane / KG;
+        const int gl = (lane % KG) ^ ((j >> 1) & (KG - 1));
+        const int64_t col = min<int64_t>(n0 + j, N - 1) - n0;
+        grpC[t] = gl;
+        offC[t] = (uint32_t)(col * (K / 2)) + (uint32_t)(gl * 16);
+        ldsC[t] = C::kABytes + q * 1024;
+    }
+#pragma unroll
+    for (int t = 0; t < C::NSW; ++t) {
+        const int q = wave * C::NSW + t;
+        if (SV) {              // lane: column j, groups 2d and 2d + 1 of the stage
+            const int piece = q * 64 + lane;
+            const int j = piece / (KG / 2), d = piece % (KG / 2);
+            const int64_t col = min<int64_t>(n0 + j, N - 1) - n0;
+            grpS[t] = 2 * d;
+            offS[t] = (uint32_t)((col * G + 2 * d) * 2);
+            ldsS[t] = C::kABytes + C::kCBytes + q * 256;
+        } else {
+            const int slot = q * 64 + lane;
+            const int gl = slot / C::BN, j = slot % C::BN;
+            const int64_t col = min<int64_t>(n0 + j, N - 1) - n0;
+            grpS[t] = gl;
+            offS[t] = (uint32_t)((col * G + gl) * 2);
+            ldsS[t] = C::kABytes + C::kCBytes + q * 256;
+        }
+    }
+    const unsigned char* xbase = reinterpret_cast<const unsigned char*>(x + m0 * K);
+    const unsigned char* cbase = packed + n0 * (K / 2);
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(scales + n0 * G);
+
+    // Loads of stage st into ring buffer buf.  With TAIL (G not a multiple
+    // of KG), groups past G in the last stage re-read group G - 1 (in bounds;
+    // their results are not used): the step back is a per-lane select, so the
+    // loop has no branch here.
+    auto issue = [&](int st, int buf) {
+        unsigned char* sb = smem + buf * C::kStage;
+        const int g0 = st * KG;
+        const int over = g0 - (G - 1);                    // > -KG only in the last stage
+        auto step_back = [&](int grp, uint32_t unit) {
+            return TAIL ? (uint32_t)max(0, over + grp) * unit : 0u;
+        };
+#pragma unroll
+        for (int t = 0; t < C::NAW; ++t) {
+            const uint32_t back = step_back((int)grpA[t], 64u);
+            __builtin_amdgcn_global_load_lds(xbase + (size_t)g0 * 64 + (offA[t] - back),
+                                             (lds_void_t*)(sb + ldsA[t]), 16, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < C::NCW; ++t) {
+            const uint32_t back = step_back((int)grpC[t], 16u);
+            __builtin_amdgcn_global_load_lds(cbase + (size_t)g0 * 16 + (offC[t] - back),
+                                             (lds_void_t*)(sb + ldsC[t]), 16, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < C::NSW; ++t) {
+            if (SV) {
+                // G is even here, so a pair never straddles G
+                const uint32_t back = step_back((int)grpS[t], 2u);
+                __builtin_amdgcn_global_load_lds(sbase + (size_t)g0 * 2 + (offS[t] - back),
+                                                 (lds_void_t*)(sb + ldsS[t]), 4, 0, 0);
+            } else {
+                const uint32_t back = step_back((int)grpS[t], 2u);
+                __builtin_amdgcn_global_load_lds(sbase + (size_t)g0 * 2 + (offS[t] - back),
+                                                 (lds_void_t*)(sb + ldsS[t]), 2, 0, 0);
+            }
+        }
+    };
+
+    // ---- per-lane operand offsets inside a stage ----
+    int rA[C::GPW][2], rC[C::GPW], rS[C::GPW];
+#pragma unroll
+    for (int u = 0; u < C::GPW; ++u) {
+        const int gl = wk + WK * u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            rA[u][h] = li * C::kRowBytes + (((gl * 4 + 2 * lg + h) ^ (li & 7)) * 16);
+        const int j = 32 * NB * wn + li;
+        rC[u] = C::kABytes + j * C::kColBytes + ((gl ^ ((li >> 1) & (KG - 1))) * 16) + 8 * lg;
+        rS[u] = C::kABytes + C::kCBytes + (SV ? (j * KG + gl) * 2 : (gl * C::BN + j) * 4);
+    }
+
+    float16v_t acc[MB][NB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rb][nb][v] = 0.f;
+
+    const uint32_t mask = kc.mask;
+    const uint32_t magic = to_vgpr(kc.magic);
+    const uint32_t sel[4] = {kc.sel[0], kc.sel[1], kc.sel[2], kc.sel[3]};
+
+    // Operands of group u of this wave from stage buffer sb: activations of
+    // the MB row blocks, unpacked levels of the NB column blocks, scales.
+    struct Ops {
+        half8_t a[MB][2];
+        half8_t b[NB][2];
+        float s[NB];
+    };
+    auto read_ops = [&](Ops& o, uint32_t (&cd)[NB][2], const unsigned char* sb, int u) {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                o.a[rb][h] =
+                    *reinterpret_cast<const half8_t*>(sb + rA[u][h] + rb * 32 * C::kRowBytes);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint2 c2 = *reinterpret_cast<const uint2*>(sb + rC[u] + nb * 32 * C::kColBytes);
+            cd[nb][0] = c2.x;
+            cd[nb][1] = c2.y;
+            // widened once and passed through an identity DPP move: the FMAs
+            // below then take a plain fp32 operand (v_fmac_f32) instead of
+            // converting the fp16 scale inside each one (v_fma_mix_f32, ~13%
+            // slower)
+            const float sf =
+                (float)*reinterpret_cast<const _Float16*>(sb + rS[u] + nb * (SV ? 64 * KG : 128));
+            o.s[nb] = __builtin_bit_cast(
+                float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sf), 0xE4, 0xF, 0xF, false));
+        }
+    };
+    auto unpack_ops = [&](Ops& o, const uint32_t (&cd)[NB][2]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) o.b[nb][h] = unpack8_natural(cd[nb][h], mask, magic, sel);
+    };
+    auto mfma2 = [&](const Ops& o, int rb, int nb) {
+        const float16v_t zero = {};
+        float16v_t p = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[rb][0], o.b[nb][0], zero, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[rb][1], o.b[nb][1], p, 0, 0, 0);
+    };
+    auto scale_add = [&](float16v_t& dst, float s, const float16v_t& p) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[v] = fmaf(s, p[v], dst[v]);
+    };
+
+    // One stage, software-pipelined: the MFMAs of a block are issued before
+    // the scale FMAs of the block before it, so the matrix core and the VALU
+    // work at once within the wave.  The last block's product (pc, scale sc,
+    // destination acc[MB - 1][NB - 1]) is carried into the next stage.
+    // The loads of a later stage (nxt into ring buffer nbuf) are issued after
+    // the first block, so their issue overlaps compute instead of every wave
+    // queueing its loads at once right after the barrier.
+    auto stage = [&](const unsigned char* sb, float16v_t& pc, float& sc, int nxt, int nbuf) {
+        Ops ops[2];
+        uint32_t cd[2][NB][2];
+        read_ops(ops[0], cd[0], sb, 0);
+        unpack_ops(ops[0], cd[0]);
+#pragma unroll
+        for (int u = 0; u < C::GPW; ++u) {
+            Ops& o = ops[u & 1];
+            if (u + 1 < C::GPW) read_ops(ops[(u + 1) & 1], cd[(u + 1) & 1], sb, u + 1);
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    if (u == 0 && rb * NB + nb == 1) issue(nxt, nbuf);
+                    const float16v_t p = mfma2(o, rb, nb);
+                    // the block before this one
+                    const int prev = rb * NB + nb - 1;
+                    if (prev < 0)
+                        scale_add(acc[MB - 1][NB - 1], sc, pc);
+                    else
+                        scale_add(acc[prev / NB][prev % NB], o.s[prev % NB], pc);
+                    pc = p;
+                    // keep this order: left alone the scheduler hoists every
+                    // MFMA of the unrolled stages ahead of the FMAs, holding
+                    // many products in registers at once
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            sc = o.s[NB - 1];
+            if (u + 1 < C::GPW) unpack_ops(ops[(u + 1) & 1], cd[(u + 1) & 1]);
+        }
+    };
+
+    // one group u of this wave, not pipelined (last stages)
+    auto group = [&](const unsigned char* sb, int u) {
+        Ops o;
+        uint32_t cd[NB][2];
+        read_ops(o, cd, sb, u);
+        unpack_ops(o, cd);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) scale_add(acc[rb][nb], o.s[nb], mfma2(o, rb, nb));
+    };
+
+    // Every iteration issues one stage's loads (stages past the end re-load
+    // the last one into a buffer nobody reads again), so stage st has landed
+    // once at most S - 2 later stages' loads remain in flight; after the
+    // barrier every wave's loads of it have landed, and every wave is done
+    // with the buffer that the refill overwrites.
+    auto wait_stage = [&]() {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kLoadsPerWave * (S - 2)));
+        barrier_keep_loads();
+    };
+
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u) issue(min(u, nstages - 1), u);
+
+    // full stages, S at a time (ring buffers at fixed offsets, no branch
+    // inside, so the pipelined order above holds)
+    const int nfull = G / KG;
+    int st = 0;
+    float16v_t pc = {};
+    float sc = 0.f;
+    for (; st + S <= nfull; st += S) {
+#pragma unroll
+        for (int b = 0; b < S; ++b) {
+            wait_stage();
+            stage(smem + b * C::kStage, pc, sc, min(st + b + S - 1, nstages - 1), (b + S - 1) % S);
+        }
+    }
+    // the other full stages (fewer than S)
+    for (; st < nfull; ++st) {
+        const int b = st % S;
+        wait_stage();
+        stage(smem + b * C::kStage, pc, sc, min(st + S - 1, nstages - 1), (b + S - 1) % S);
+    }
+    scale_add(acc[MB - 1][NB - 1], sc, pc);
+    // a partial last stage (G not a multiple of KG)
+    if (nfull < nstages) {
+        const int b = nfull % S;
+        wait_stage();
+        const unsigned char* sb = smem + b * C::kStage;
+#pragma unroll
+        for (int u = 0; u < C::GPW; ++u)
+            if (nfull * KG + wk + WK * u < G) group(sb, u);
+    }
+
+    // ---- add the WK partial tiles (fixed order) and store ----
+    // Waves of K phases 1..WK-1 park their partial tiles in LDS; phase 0
+    // adds them in phase order; the final tile goes to LDS row-major and all
+    // waves store it, 16 bytes per lane where the rows allow.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    constexpr int kPart = MB * NB * 16 * 64;             // floats of one wave's partial
+    if (wk > 0) {
+        float* dst = red + ((wk - 1) * WN + wn) * kPart + lane;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dst[((rb * NB + nb) * 16 + v) * 64] = acc[rb][nb][v];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+        for (int q = 1; q < WK; ++q) {
+            const float* src = red + ((q - 1) * WN + wn) * kPart + lane;
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[rb][nb][v] += src[((rb * NB + nb) * 16 + v) * 64];
+        }
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    red[(32 * rb + 8 * (v >> 2) + 4 * lg + (v & 3)) * C::BN + 32 * NB * wn + 32 * nb +
+                        li] = acc[rb][nb][v];
+    }
+    __syncthreads();
+    // row-major tile: BM rows x BN / 4 four-float pieces
+    for (int i = threadIdx.x; i < C::BM * C::BN / 4; i += C::kThreads) {
+        const int r = i / (C::BN / 4), c = 4 * (i % (C::BN / 4));
+        const int64_t m = m0 + r, n = n0 + c;
+        if (m >= M) continue;
+        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(red + r * C::BN + c);
+        float* out = y + m * N + n;
+        if (vec_store && n + 3 < N) {
+            *reinterpret_cast<f32x4_t*>(out) = t;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) out[e] = t[e];
+        }
+    }
+}
+
+template <int MB, int NB, int WN, int WK, int KG, int S, bool SV, bool TAIL>
+hipError_t launch_gemm32_grid(const uint16_t* x, const GemmSegments& seg, int64_t tiles,
+                              int64_t m, int64_t k, int vec, hipStream_t stream) {
+    using C = G32<MB, NB, WN, WK, KG, S, SV>;
+    static std::atomic<uint64_t> lds_done{0};
+    hipError_t e = allow_dynamic_lds(
+        reinterpret_cast<const void*>(&gemm32_kernel<MB, NB, WN, WK, KG, S, SV, TAIL>), C::kLds,
+        lds_done);
+    if (e != hipSuccess) return e;
+    for (int64_t base = 0; base < tiles; base += kGemmMaxGrid) {
+        const int64_t grid = tiles - base < kGemmMaxGrid ? tiles - base : kGemmMaxGrid;
+        hipLaunchKernelGGL((gemm32_kernel<MB, NB, WN, WK, KG, S, SV, TAIL>), dim3((unsigned)grid),
+                           dim3(C::kThreads), C::kLds, stream, x, seg, (int)m, (int)k,
+                           (int)(k / 32), kSpliceConsts, base, vec);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// whether the 4-byte scale loads split evenly over the waves of a shape
+template <int MB, int NB, int WN, int WK, int KG, int S>
+struct SvOk {
+    static constexpr bool value = KG % 2 == 0 && (32 * NB * WN * KG / 128) % (WN * WK) == 0;
+};
+
+template <int MB, int NB, int WN, int WK, int KG, int S>
+hipError_t launch_gemm32_t(const uint16_t* x, int count, const uint8_t* const* packed,
+                           const uint16_t* const* scales, float* const* y, const int64_t* n,
+                           int64_t m, int64_t k, hipStream_t stream) {
+    GemmSegments seg = {};
+    seg.count = count;
+    int64_t tiles = 0;
+    constexpr int BM = 32 * MB, BN = 32 * NB * WN;
+    // 4-byte scale loads (two groups per lane): every pair 4-byte aligned, and
+    // as many of them per stage as there are waves
+    bool sv = SvOk<MB, NB, WN, WK, KG, S>::value && (k / 32) % 2 == 0;
+    // 16-byte stores: every row of every output 16-byte aligned
+    int vec = 1;
+    for (int i = 0; i < count; ++i) {
+        seg.packed[i] = packed[i];
+        seg.scales[i] = scales[i];
+        seg.y[i] = y[i];
+        seg.n[i] = n[i];
+        seg.tiles_n[i] = (n[i] + BN - 1) / BN;
+        seg.tile0[i] = tiles;
+        tiles += seg.tiles_n[i] * ((m + BM - 1) / BM);
+        sv = sv && (reinterpret_cast<uintptr_t>(scales[i]) % 4) == 0;
+        if ((reinterpret_cast<uintptr_t>(y[i]) % 16) != 0 || n[i] % 4 != 0) vec = 0;
+    }
+    constexpr bool kSv = SvOk<MB, NB, WN, WK, KG, S>::value;
+    if ((k / 32) % KG != 0)
+        return launch_gemm32_grid<MB, NB, WN, WK, KG, S, false, true>(x, seg, tiles, m, k, vec,
+                                                                      stream);
+    if (sv) return launch_gemm32_grid<MB, NB, WN, WK, KG, S, kSv, false>(x, seg, tiles, m, k, vec,
+                                                                          stream);
+    return launch_gemm32_grid<MB, NB, WN, WK, KG, S, false, false>(x, seg, tiles, m, k, vec,
+                                                                   stream);
+}
+
 // Tile shapes for m > 32, largest first, with the time one full round of
-// them takes (k = 2560, n = 4096, one tile per CU; measured).
+// them takes (k = 2560, n = 4096, one tile per CU; measured on MI355X over
+// m = 128 ... 2048: the 32 x 32 block kernel from m = 384 on, the 16 x 16
+// block tiles below).
 constexpr TileChoice kTiles[] = {
-    {128, 128, 35.f},      // gemm_kernel<128, 4, 2, 2, 2>
-    {64, 128, 22.f},       // gemm_kernel<64, 4, 4, 2, 2> (16 waves)
-    {64, 64, 15.5f},       // gemm_kernel<64, 2, 4, 2, 2>
-    {32, 64, 11.f},        // gemm_kernel<32, 2, 4, 2, 2>
+    {128, 128, 35.f},      // gemm32_kernel<4, 1, 4, 2, 4, 3>: 4 column slices x 2 K phases
+    {64, 128, 20.f},       // gemm32_kernel<2, 2, 2, 4, 8, 2>: 2 column slices x 4 K phases
+    {64, 64, 16.f},        // gemm_kernel<64, 2, 4, 2, 2>
+    {32, 64, 15.f},        // gemm_kernel<32, 2, 4, 2, 2>
 };
 
 hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* const* packed,
@@ -406,8 +877,8 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
     const hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     switch (choose_tile(kTiles, 4, m, count, n, device_info(dev).cu_count)) {
-        case 0: return launch_gemm_t<128, 4, 2, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
-        case 1: return launch_gemm_t<64, 4, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+        case 0: return launch_gemm32_t<4, 1, 4, 2, 4, 3>(x, count, packed, scales, y, n, m, k, stream);
+        case 1: return launch_gemm32_t<2, 2, 2, 4, 8, 2>(x, count, packed, scales, y, n, m, k, stream);
         case 2: return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
         default: return launch_gemm_t<32, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
     }

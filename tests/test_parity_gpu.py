@@ -163,15 +163,17 @@ def test_prefill_product(q4, orc, m, n, k):
     assert_within(y, y_ref, bound, "q4_gemm m=%d n=%d k=%d" % (m, n, k))
 
 
-TILING_CASES = [(64, 1000, 256), (256, 4096, 256), (384, 4096, 128), (520, 4100, 160),
-                (1030, 4100, 96)]
+TILING_CASES = [(64, 1000, 256), (256, 4096, 256), (384, 4096, 128), (512, 4096, 256),
+                (520, 4100, 160), (1024, 4096, 256), (600, 4098, 96), (1030, 4100, 96)]
 
 
 @pytest.mark.parametrize("m,n,k", TILING_CASES, ids=["m%d-n%d-k%d" % c for c in TILING_CASES])
 def test_prefill_every_tile_shape(q4, orc, m, n, k):
     """Shapes for which the GEMM picks each of its tile shapes on a 256-CU
-    device (32x64, 64x64, 64x128, 128x128, and 64x128 with ragged rows and
-    columns), compared in full."""
+    device, compared in full: 32x64 and 64x64 (16x16 blocks); 64x128 (32x32
+    blocks) with a group count that is and is not a multiple of its 8-group
+    stage; 128x128 (32x32 blocks) with and without a partial last stage, with
+    ragged rows and columns, and with n % 4 != 0 (element-wise stores)."""
     x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m + n + k)
     _log("q4_gemm m=%d n=%d k=%d" % (m, n, k))
     y = product(q4, "q4_gemm", x, packed, scales)
@@ -191,21 +193,23 @@ def test_blockdiag_lds_limits(q4, orc, m, n, k):
     assert_within(y, y_ref, bound, "q4_gemv m=%d n=%d k=%d" % (m, n, k))
 
 
-SCALE_OFFSET_CASES = [("q4_gemv", 1, 1024), ("q4_gemv", 2, 1024), ("q4_gemv", 5, 544),
-                      ("q4_gemv", 8, 7936), ("q4_gemv", 3, 16384), ("q4_gemm", 40, 1024),
-                      ("q4_gemm", 16, 1056), ("q4_gemm", 32, 1056)]
+SCALE_OFFSET_CASES = [("q4_gemv", 1, 1024, 37), ("q4_gemv", 2, 1024, 37),
+                      ("q4_gemv", 5, 544, 37), ("q4_gemv", 8, 7936, 37),
+                      ("q4_gemv", 3, 16384, 37), ("q4_gemm", 40, 1024, 37),
+                      ("q4_gemm", 16, 1056, 37), ("q4_gemm", 32, 1056, 37),
+                      ("q4_gemm", 512, 256, 4096), ("q4_gemm", 1024, 256, 4096)]
 
 
-@pytest.mark.parametrize("fn,m,k", SCALE_OFFSET_CASES,
-                         ids=["%s-m%d-k%d" % c for c in SCALE_OFFSET_CASES])
+@pytest.mark.parametrize("fn,m,k,n", SCALE_OFFSET_CASES,
+                         ids=["%s-m%d-k%d-n%d" % c for c in SCALE_OFFSET_CASES])
 @pytest.mark.parametrize("offset", [1, 2, 4, 8])
-def test_scales_at_any_even_address(q4, orc, fn, m, k, offset):
+def test_scales_at_any_even_address(q4, orc, fn, m, k, n, offset):
     """The scale matrix need only be 2-byte aligned: it is placed `offset`
     fp16 elements past a 256-byte boundary (2, 4, 8 and 16 bytes), so the
-    kernels whose wide scale loads need 8 or 16 bytes (m = 2..8 with a whole
-    number of steps or tiles) must take their 2-byte form there.  Every
-    offset gives the bits of the aligned call."""
-    n = 37
+    kernels whose wide scale loads need 4, 8 or 16 bytes (m = 2..8 with a
+    whole number of steps or tiles; the 64x128 and 128x128 GEMM tiles) must
+    take their 2-byte form there.  Every offset gives the bits of the
+    aligned call."""
     x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m + k + offset)
     _log("%s m=%d n=%d k=%d scales at +%d B" % (fn, m, n, k, 2 * offset))
     y0 = product(q4, fn, x, packed, scales)
@@ -388,7 +392,9 @@ GEMM_MULTI_SETS = [
     (128, 2560, (130, 5, 257, 64)),
     (300, 96, (17, 200, 3, 1, 70, 33, 9, 129)),            # eight matrices
     (512, 1024, (100, 61)),
-    (1030, 256, (130, 61, 257)),                           # 128 x 128 tiles
+    (1030, 256, (130, 61, 257)),                           # 64 x 64 tiles
+    (512, 256, (2048, 1000, 777)),                         # 64 x 128 tiles (32x32 blocks)
+    (1024, 160, (4096, 130, 3000)),                        # 128 x 128 tiles, partial stage
     (3, 256, (15, 100)),                                   # m <= 8: the q4_gemv_multi path
 ]
 
