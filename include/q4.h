@@ -119,7 +119,9 @@ q4_status q4_gemv(const uint16_t* x, const uint8_t* packed,
  * the QORA-LLM-0.8B card ("AVX-512 SIMD Acceleration"), and the q/k/v
  * projections of one layer input in the hybrid DeltaNet/attention stack
  * ("Architecture" table of the same card).  One launch serves the whole set
- * at m = 1, so the fixed cost of a kernel is paid once, not per matrix.
+ * (m = 1..8; at m >= 2 with k above 7680, or 15360 for m <= 4, where the
+ * activations no longer fit the LDS at once, one launch per matrix), so the
+ * fixed cost of a kernel is paid once, not per matrix.
  *   x       [in]  fp16 bits [m, k], device, 1 <= m <= 8
  *   count         number of matrices, 1 .. Q4_MULTI_MAX
  *   packed  [in]  HOST array of count device pointers, uint8 [n[i], k/2]

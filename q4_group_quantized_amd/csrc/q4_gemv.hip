@@ -28,7 +28,8 @@
 //
 // Activations are staged once per workgroup in LDS, permuted inside every
 // 8-element chunk to the order unpack8_fma produces codes in, so A and B agree
-// element by element.  Scales are read as 8 consecutive fp16 per lane (one
+// element by element; several matrices over the same x (q4_gemv_multi) share
+// one launch, their waves split in proportion to their rows.  Scales are read as 8 consecutive fp16 per lane (one
 // 16-byte load when G % 8 == 0 and the scale matrix is 16-byte aligned, else
 // eight 2-byte loads).
 //
@@ -191,23 +192,48 @@ constexpr int kStepGroups = 16;
 constexpr int kStepCodeBytes = 16 * 256;
 constexpr int kStepBytes = kStepCodeBytes + 16 * 32;      // codes + scales of a step
 
+// The matrices of one flat launch (q4_gemv: one; q4_gemv_multi: up to
+// kFlatMaxSegments sharing x and K).  Matrix s owns the waves
+// [w0[s], w0[s] + wn[s]) of the grid, which split its row blocks evenly.
+constexpr int kFlatMaxSegments = 8;
+struct FlatSegments {
+    const uint8_t* packed[kFlatMaxSegments];
+    const uint16_t* scales[kFlatMaxSegments];
+    float* y[kFlatMaxSegments];
+    int64_t n[kFlatMaxSegments];
+    int64_t w0[kFlatMaxSegments];
+    int64_t wn[kFlatMaxSegments];
+    int count;
+};
+static_assert(kFlatMaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MULTI_MAX matrices");
+
 template <int TB, bool kWhole16>
 __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
-                                          const uint8_t* __restrict__ packed,
-                                          const uint16_t* __restrict__ scales,
-                                          float* __restrict__ y, _Float16* xs,
-                                          unsigned char* step_bufs, int M, int64_t N, int K,
-                                          int G, int64_t RB, const SpliceConsts& kc) {
+                                          const FlatSegments& seg, _Float16* xs,
+                                          unsigned char* step_bufs, int M, int K, int G,
+                                          const SpliceConsts& kc) {
     const int lane = threadIdx.x & 63;
     const int kb = lane >> 4, rr = lane & 15;             // tile layout
     const int lr = lane >> 4, lj = lane & 15;             // code loads
     const int sr = lane >> 2, sp = lane & 3;              // scale loads
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t W = (int64_t)gridDim.x * kGemvWaves;
     const int64_t w = (int64_t)blockIdx.x * kGemvWaves + wave;
+    // this wave's matrix (wave-uniform selects over constant indices)
+    const uint8_t* __restrict__ packed = seg.packed[0];
+    const uint16_t* __restrict__ scales = seg.scales[0];
+    float* __restrict__ y = seg.y[0];
+    int64_t N = seg.n[0], w0 = seg.w0[0], W = seg.wn[0];
+#pragma unroll
+    for (int i = 1; i < kFlatMaxSegments; ++i)
+        if (i < seg.count && w >= seg.w0[i]) {
+            packed = seg.packed[i]; scales = seg.scales[i]; y = seg.y[i];
+            N = seg.n[i]; w0 = seg.w0[i]; W = seg.wn[i];
+        }
+    const int64_t RB = (N + 15) / 16;
+    const int64_t lw = w - w0;                           // >= W: a spare wave, no rows
     const int64_t base = RB / W, extra = RB % W;
-    const int64_t rb_begin = w * base + (w < extra ? w : extra);
-    const int64_t count = base + (w < extra ? 1 : 0);
+    const int64_t rb_begin = lw < W ? lw * base + (lw < extra ? lw : extra) : RB;
+    const int64_t count = lw < W ? base + (lw < extra ? 1 : 0) : 0;
     const int T = ((G + 15) & ~15) / kStepGroups;        // steps per row block
     const int64_t F = count * T;                         // flat steps of this wave
     unsigned char* bufs = step_bufs + (size_t)wave * 2 * kStepBytes;
@@ -377,12 +403,11 @@ __device__ __forceinline__ void gemv_chunked(const uint16_t* __restrict__ x,
 
 template <int TB, bool kWhole16>
 __global__ __launch_bounds__(kGemvThreads, 2) void gemv_flat_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, float* __restrict__ y, int M, int64_t N, int K,
-    int G, int64_t RB, int xs_bytes, SpliceConsts kc) {
+    const uint16_t* __restrict__ x, FlatSegments seg, int M, int K, int G, int xs_bytes,
+    SpliceConsts kc) {
     extern __shared__ __align__(16) unsigned char smem[];
-    gemv_flat<TB, kWhole16>(x, packed, scales, y, reinterpret_cast<_Float16*>(smem),
-                            smem + xs_bytes, M, N, K, G, RB, kc);
+    gemv_flat<TB, kWhole16>(x, seg, reinterpret_cast<_Float16*>(smem), smem + xs_bytes, M, K,
+                            G, kc);
 }
 
 template <int TB, bool kScale16>
@@ -398,12 +423,14 @@ __global__ __launch_bounds__(kGemvThreads, 2) void gemv_kernel(
 // Whole K staged at once when the padded activations and 2 step buffers per
 // wave fit the CU's 160 KB of LDS (k <= 7680 at m = 5..8, 15360 at m <= 4):
 // two workgroups per CU where their LDS allows (measured faster than one at
-// k = 1024 and 2560), each wave with the same number of row blocks.
-// Otherwise chunked (kLdsBudget of activations per pass), as many waves as fit.
+// k = 1024 and 2560), the waves split between the matrices in proportion to
+// their row blocks, each wave of a matrix with the same number of row blocks.
+// Otherwise chunked (kLdsBudget of activations per pass), as many waves as
+// fit, one launch per matrix.
 template <int TB>
-hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
-                         const uint16_t* scales, float* y, int m, int64_t n,
-                         int k, hipStream_t stream) {
+hipError_t launch_gemv_t(const uint16_t* x, int m, int k, int count,
+                         const uint8_t* const* packed, const uint16_t* const* scales,
+                         float* const* y, const int64_t* n, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -411,19 +438,41 @@ hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
     const int G = k / 32;
     const int per_group_bytes = TB * 4 * 64;
     const int fixed_bytes = TB * 4 * kTokenPad * 2 + 64;     // token pads, zero block
-    const int64_t RB = (n + 15) / 16;
     const int64_t g16 = (G + 15) & ~15;
     const int64_t xs_bytes = (per_group_bytes * g16 + fixed_bytes + 15) & ~15;
     const size_t lds = (size_t)xs_bytes + (size_t)kGemvWaves * 2 * kStepBytes;
     if (lds <= (size_t)160 * 1024) {
         const int wgs = 2 * lds <= (size_t)160 * 1024 ? 2 : 1;
         const int64_t max_waves = (int64_t)cu * kGemvWaves * wgs;
-        const int64_t per = (RB + max_waves - 1) / max_waves;
-        const int64_t waves = (RB + per - 1) / per;
+        int64_t rb_total = 0;
+        for (int s = 0; s < count; ++s) rb_total += (n[s] + 15) / 16;
+        FlatSegments seg = {};
+        seg.count = count;
+        // 8-byte scale loads need whole steps and 8-byte aligned scale
+        // matrices (the contract only promises 2 bytes)
+        bool whole = G % 16 == 0;
+        int64_t waves = 0;
+        for (int s = 0; s < count; ++s) {
+            const int64_t rb = (n[s] + 15) / 16;
+            // this matrix's share of the resident waves, then as few waves
+            // as give every wave the same number of row blocks
+            int64_t share = (max_waves * rb + rb_total / 2) / rb_total;
+            share = share < 1 ? 1 : share;
+            const int64_t per = (rb + share - 1) / share;
+            seg.packed[s] = packed[s];
+            seg.scales[s] = scales[s];
+            seg.y[s] = y[s];
+            seg.n[s] = n[s];
+            seg.w0[s] = waves;
+            seg.wn[s] = (rb + per - 1) / per;
+            waves += seg.wn[s];
+            whole = whole && (reinterpret_cast<uintptr_t>(scales[s]) & 7) == 0;
+        }
+        if (count == 1) {
+            // one matrix: every wave of the grid takes a share
+            seg.wn[0] = (waves + kGemvWaves - 1) / kGemvWaves * kGemvWaves;
+        }
         const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
-        // 8-byte scale loads need whole steps and an 8-byte aligned scale
-        // matrix (the contract only promises 2 bytes)
-        const bool whole = G % 16 == 0 && (reinterpret_cast<uintptr_t>(scales) & 7) == 0;
         const void* fn = whole ? reinterpret_cast<const void*>(&gemv_flat_kernel<TB, true>)
                                : reinterpret_cast<const void*>(&gemv_flat_kernel<TB, false>);
         static std::atomic<uint64_t> lds_done[2] = {{0}, {0}};
@@ -431,33 +480,36 @@ hipError_t launch_gemv_t(const uint16_t* x, const uint8_t* packed,
         if (e != hipSuccess) return e;
         if (whole)
             hipLaunchKernelGGL((gemv_flat_kernel<TB, true>), dim3(blocks), dim3(kGemvThreads), lds,
-                               stream, x, packed, scales, y, m, n, k, G, RB, (int)xs_bytes,
-                               kSpliceConsts);
+                               stream, x, seg, m, k, G, (int)xs_bytes, kSpliceConsts);
         else
             hipLaunchKernelGGL((gemv_flat_kernel<TB, false>), dim3(blocks), dim3(kGemvThreads),
-                               lds, stream, x, packed, scales, y, m, n, k, G, RB, (int)xs_bytes,
-                               kSpliceConsts);
+                               lds, stream, x, seg, m, k, G, (int)xs_bytes, kSpliceConsts);
         return hipGetLastError();
     }
     const int gpad = (G + 7) & ~7;
     int chunk = ((kLdsBudget - fixed_bytes) / per_group_bytes) & ~7;
     if (chunk > gpad) chunk = gpad;
     const int nchunks = (gpad + chunk - 1) / chunk;
-    // resident waves: 4 per SIMD, 4 SIMDs per CU
-    const int64_t max_waves = (int64_t)cu * 16;
-    const int64_t waves = RB < max_waves ? RB : max_waves;
-    const int64_t blocks64 = (waves + kGemvWaves - 1) / kGemvWaves;
-    const int blocks = (int)(blocks64 > 0 ? blocks64 : 1);
     const size_t chunk_lds = (size_t)per_group_bytes * chunk + fixed_bytes;
-    if (G % 8 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)   // 16-byte scale loads
-        hipLaunchKernelGGL((gemv_kernel<TB, true>), dim3(blocks), dim3(kGemvThreads), chunk_lds,
-                           stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB,
-                           kSpliceConsts);
-    else
-        hipLaunchKernelGGL((gemv_kernel<TB, false>), dim3(blocks), dim3(kGemvThreads), chunk_lds,
-                           stream, x, packed, scales, y, m, n, k, G, chunk, nchunks, RB,
-                           kSpliceConsts);
-    return hipGetLastError();
+    for (int s = 0; s < count; ++s) {
+        const int64_t RB = (n[s] + 15) / 16;
+        // resident waves: 4 per SIMD, 4 SIMDs per CU
+        const int64_t max_waves = (int64_t)cu * 16;
+        const int64_t waves = RB < max_waves ? RB : max_waves;
+        const int64_t blocks64 = (waves + kGemvWaves - 1) / kGemvWaves;
+        const int blocks = (int)(blocks64 > 0 ? blocks64 : 1);
+        if (G % 8 == 0 && (reinterpret_cast<uintptr_t>(scales[s]) & 15) == 0)   // 16-byte scale loads
+            hipLaunchKernelGGL((gemv_kernel<TB, true>), dim3(blocks), dim3(kGemvThreads),
+                               chunk_lds, stream, x, packed[s], scales[s], y[s], m, n[s], k, G,
+                               chunk, nchunks, RB, kSpliceConsts);
+        else
+            hipLaunchKernelGGL((gemv_kernel<TB, false>), dim3(blocks), dim3(kGemvThreads),
+                               chunk_lds, stream, x, packed[s], scales[s], y[s], m, n[s], k, G,
+                               chunk, nchunks, RB, kSpliceConsts);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -745,11 +797,11 @@ hipError_t launch_gemv1(const uint16_t* x, int k, int count, const uint8_t* cons
     }
 }
 
-hipError_t launch_gemv_blockdiag(const uint16_t* x, const uint8_t* packed,
-                                 const uint16_t* scales, float* y, int64_t m, int64_t n,
-                                 int64_t k, hipStream_t stream) {
-    if (m <= 4) return launch_gemv_t<1>(x, packed, scales, y, (int)m, n, (int)k, stream);
-    return launch_gemv_t<2>(x, packed, scales, y, (int)m, n, (int)k, stream);
+hipError_t launch_gemv_blockdiag(const uint16_t* x, int64_t m, int64_t k, int count,
+                                 const uint8_t* const* packed, const uint16_t* const* scales,
+                                 float* const* y, const int64_t* n, hipStream_t stream) {
+    if (m <= 4) return launch_gemv_t<1>(x, (int)m, (int)k, count, packed, scales, y, n, stream);
+    return launch_gemv_t<2>(x, (int)m, (int)k, count, packed, scales, y, n, stream);
 }
 
 }  // namespace
@@ -759,7 +811,7 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed,
                        int64_t k, hipStream_t stream) {
     if (m == 1 && gemv1_lanes_per_row(k) != 0)
         return launch_gemv1(x, (int)k, 1, &packed, &scales, &y, &n, nullptr, stream);
-    return launch_gemv_blockdiag(x, packed, scales, y, m, n, k, stream);
+    return launch_gemv_blockdiag(x, m, k, 1, &packed, &scales, &y, &n, stream);
 }
 
 int64_t gemv1_topk_lists(int64_t n, int64_t k, int cu_count) {
@@ -786,11 +838,7 @@ hipError_t launch_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int count,
                              float* const* y, const int64_t* n, hipStream_t stream) {
     if (m == 1 && gemv1_lanes_per_row(k) != 0)
         return launch_gemv1(x, (int)k, count, packed, scales, y, n, nullptr, stream);
-    for (int s = 0; s < count; ++s) {
-        const hipError_t e = launch_gemv_blockdiag(x, packed[s], scales[s], y[s], m, n[s], k, stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return launch_gemv_blockdiag(x, m, k, count, packed, scales, y, n, stream);
 }
 
 }  // namespace q4

@@ -343,6 +343,12 @@ MULTI_SETS = [
     (1, 96, (17, 33)),                               # k outside the streaming kernel
     (2, 256, (15, 100)),
     (8, 1056, (33, 7, 64)),
+    (4, 2560, (61, 5, 1000, 3, 257, 64, 9, 2)),      # m <= 4 tile, eight matrices
+    (5, 1024, (1, 17, 300, 4099)),
+    (8, 2560, (2048, 2048, 4096)),                   # 4B DeltaNet q/k/v rows
+    (7, 96, (17, 33)),                               # G = 3: partial step
+    (8, 8192, (5, 61, 700)),                         # activations too large: chunked
+    (3, 16384, (40, 3)),
 ]
 
 
@@ -367,6 +373,36 @@ def test_gemv_multi(q4, orc, m, k, ns):
         assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound,
                       "multi matrix %d (n=%d)" % (i, ns[i]))
         alone = q4.q4_gemv(xg, *mats[i])
+        torch.cuda.synchronize()
+        assert torch.equal(y, alone), "multi matrix %d differs from q4_gemv" % i
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_gemv_multi_mixed_scale_alignment(q4, orc, m):
+    """One matrix of the set has its scales only 2-byte aligned, so the whole
+    launch takes the 2-byte scale loads; every output keeps the bits of
+    q4_gemv on that matrix alone (which takes the wide loads where it can)."""
+    rng = np.random.default_rng(90 + m)
+    k, ns = 1024, (100, 2048, 33)
+    x = (rng.standard_normal((m, k)) * 2).astype(np.float16)
+    xg = gpu(x)
+    mats, refs = [], []
+    for i, n in enumerate(ns):
+        packed, scales = orc.quantize((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+        sg = gpu(scales.view(np.float16))
+        if i == 1:
+            buf = torch.zeros(sg.numel() + 16, dtype=torch.float16, device=DEV)
+            sg = buf[1:1 + sg.numel()].view(sg.shape)
+            sg.copy_(gpu(scales.view(np.float16)))
+            assert sg.data_ptr() % 8 == 2
+        mats.append((gpu(packed), sg))
+        refs.append(orc.matmul(x, packed, scales))
+    _log("q4_gemv_multi m=%d k=%d n=%s, scales of matrix 1 at +2 B" % (m, k, ns))
+    ys = q4.q4_gemv_multi(xg, mats)
+    torch.cuda.synchronize()
+    for i, (y, (y_ref, bound)) in enumerate(zip(ys, refs)):
+        assert_within(y.cpu().numpy().astype(np.float64), y_ref, bound, "matrix %d" % i)
+        alone = q4.q4_gemv(xg, mats[i][0], mats[i][1].clone())   # aligned copy
         torch.cuda.synchronize()
         assert torch.equal(y, alone), "multi matrix %d differs from q4_gemv" % i
 
