@@ -442,8 +442,9 @@ struct G32 {
     static constexpr int NS = SV ? BN * KG / 128 : KG * BN / 64;
     static constexpr int NAW = NA / W, NCW = NC / W, NSW = NS / W;
     static constexpr int kLoadsPerWave = NAW + NCW + NSW;
-    // partial tiles of K phases 1..WK-1, then the final tile row-major
-    static constexpr int kRedBytes = (WK > 1 ? WK - 1 : 1) * BM * BN * 4;
+    // the WK partial tiles, row-major with rows of RS floats
+    static constexpr int RS = BN + 4;
+    static constexpr int kRedBytes = WK * BM * RS * 4;
     static constexpr int kLds = S * kStage > kRedBytes ? S * kStage : kRedBytes;
     static constexpr int CPR = 4 * KG;                   // 16-byte chunks per activation row
     static constexpr int RPI = 64 / CPR;                 // rows per load instruction
@@ -737,45 +738,24 @@ __global__ __launch_bounds__(64 * WN * WK, 1) void gemm32_kernel(
     }
 
     // ---- add the WK partial tiles (fixed order) and store ----
-    // Waves of K phases 1..WK-1 park their partial tiles in LDS; phase 0
-    // adds them in phase order; the final tile goes to LDS row-major and all
-    // waves store it, 16 bytes per lane where the rows allow.
+    // Every wave parks its partial tile row-major in LDS (partial wk at
+    // red + wk * BM * RS, rows padded to RS floats so the two lane halves of
+    // a write hit different banks); then every thread adds the WK partials of
+    // its 4-float pieces in phase order 0, 1, ..., WK - 1 and stores them, 16
+    // bytes per lane where the rows allow.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     float* red = reinterpret_cast<float*>(smem);
-    constexpr int kPart = MB * NB * 16 * 64;             // floats of one wave's partial
-    if (wk > 0) {
-        float* dst = red + ((wk - 1) * WN + wn) * kPart + lane;
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) dst[((rb * NB + nb) * 16 + v) * 64] = acc[rb][nb][v];
-    }
-    __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-        for (int q = 1; q < WK; ++q) {
-            const float* src = red + ((q - 1) * WN + wn) * kPart + lane;
-#pragma unroll
-            for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[rb][nb][v] += src[((rb * NB + nb) * 16 + v) * 64];
-        }
-    }
-    __syncthreads();
-    if (wk == 0) {
+    {
+        float* dst = red + wk * C::BM * C::RS + 32 * NB * wn + li;
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    red[(32 * rb + 8 * (v >> 2) + 4 * lg + (v & 3)) * C::BN + 32 * NB * wn + 32 * nb +
-                        li] = acc[rb][nb][v];
+                    dst[(32 * rb + 8 * (v >> 2) + 4 * lg + (v & 3)) * C::RS + 32 * nb] =
+                        acc[rb][nb][v];
     }
     __syncthreads();
     // row-major tile: BM rows x BN / 4 four-float pieces
@@ -783,7 +763,10 @@ __global__ __launch_bounds__(64 * WN * WK, 1) void gemm32_kernel(
         const int r = i / (C::BN / 4), c = 4 * (i % (C::BN / 4));
         const int64_t m = m0 + r, n = n0 + c;
         if (m >= M) continue;
-        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(red + r * C::BN + c);
+        f32x4_t t = *reinterpret_cast<const f32x4_t*>(red + r * C::RS + c);
+#pragma unroll
+        for (int q = 1; q < WK; ++q)
+            t += *reinterpret_cast<const f32x4_t*>(red + q * C::BM * C::RS + r * C::RS + c);
         float* out = y + m * N + n;
         if (vec_store && n + 3 < N) {
             *reinterpret_cast<f32x4_t*>(out) = t;

@@ -138,20 +138,34 @@ __device__ __forceinline__ void compute_tile(const Tile& t, const _Float16* xs,
 
 // Stage activations of groups [jc0, jc0 + cg) of all TB*4 token slots into
 // LDS, permuted to unpack order; tokens >= M and groups >= G are zero.
+// Loads are issued kStageBatch at a time before any of them is written, so a
+// thread waits for one round trip per batch rather than one per 16 bytes
+// (at k = 2560 and m = 8 a thread moves ten units; staged one by one they
+// cost several microseconds before the first product).
+constexpr int kStageBatch = 8;
+
 template <int TB>
 __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, _Float16* xs, int M,
                                         int K, int G, int jc0, int cg) {
     const int units = TB * 4 * cg * 4;                  // 16-byte units
-    for (int u = threadIdx.x; u < units; u += kGemvThreads) {
-        const int q = u & 3;
-        const int jl = (u >> 2) % cg;
-        const int tok = (u >> 2) / cg;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        const int j = jc0 + jl;
-        if (tok < M && j < G)
-            v = *reinterpret_cast<const u32x4_t*>(x + (size_t)tok * K + 32 * j + 8 * q);
-        *reinterpret_cast<u32x4_t*>(xs + (size_t)tok * (cg * 32 + kTokenPad) + jl * 32 + 8 * q) =
-            permute_x8(v);
+    for (int u0 = threadIdx.x; u0 < units; u0 += kStageBatch * kGemvThreads) {
+        u32x4_t v[kStageBatch];
+        int off[kStageBatch];
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b) {
+            const int u = u0 + b * kGemvThreads;
+            const int q = u & 3;
+            const int jl = (u >> 2) % cg;
+            const int tok = (u >> 2) / cg;
+            const int j = jc0 + jl;
+            v[b] = u32x4_t{0u, 0u, 0u, 0u};
+            if (u < units && tok < M && j < G)
+                v[b] = *reinterpret_cast<const u32x4_t*>(x + (size_t)tok * K + 32 * j + 8 * q);
+            off[b] = u < units ? tok * (cg * 32 + kTokenPad) + jl * 32 + 8 * q : -1;
+        }
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b)
+            if (off[b] >= 0) *reinterpret_cast<u32x4_t*>(xs + off[b]) = permute_x8(v[b]);
     }
     if (threadIdx.x < 4)
         *reinterpret_cast<u32x4_t*>(xs + (size_t)TB * 4 * (cg * 32 + kTokenPad) + 8 * threadIdx.x) =
