@@ -736,6 +736,17 @@ constexpr int gemv1_prefetch(int gpl) {
 }
 constexpr int gemv1_waves_per_simd(int gpl) { return gpl <= 3 ? 2 : 1; }
 
+// Waves per SIMD of a launch over `steps` steps: the table's value, except
+// that a second wave per SIMD is only used when every wave still gets two
+// steps or more -- with one step per wave the fixed cost of a wave (its
+// activation loads, the first load round trip) is not amortised, and one
+// wave per SIMD with two steps each was faster (k = 1024, n = 6144: 4.38
+// against 4.84 us; from n = 16384 rows at k = 1024 on the two are within 2%).
+int gemv1_wps(int gpl, int64_t steps, int cu_count) {
+    const int wps = gemv1_waves_per_simd(gpl);
+    return wps > 1 && steps < 2 * (int64_t)cu_count * kGemvWaves * wps ? 1 : wps;
+}
+
 template <int LPR, int GPL>
 hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* const* packed,
                           const uint16_t* const* scales, float* const* y, const int64_t* n,
@@ -749,8 +760,8 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
     seg.count = count;
     int64_t total_rq = 0;
     for (int s = 0; s < count; ++s) total_rq += (n[s] + RPS - 1) / RPS;
-    const int wps = gemv1_waves_per_simd(GPL);
-    const int64_t max_waves = (int64_t)device_info(dev).cu_count * kGemvWaves * wps;
+    const int cu = device_info(dev).cu_count;
+    const int64_t max_waves = (int64_t)cu * kGemvWaves * gemv1_wps(GPL, total_rq, cu);
     const int64_t per = (total_rq + max_waves - 1) / max_waves;   // steps per wave
     int64_t wave0 = 0;
     for (int s = 0; s < count; ++s) {
@@ -832,10 +843,11 @@ int64_t gemv1_topk_lists(int64_t n, int64_t k, int cu_count) {
     const int lpr = gemv1_lanes_per_row(k);
     if (lpr == 0) return 0;
     // the m = 1 launcher's grid for one matrix of n rows (launch_gemv1_t):
-    // waves per SIMD from the groups per lane, rounded up to whole workgroups
+    // waves per SIMD from the groups per lane and the steps, rounded up to
+    // whole workgroups
     const int gpl = (int)((k / 32) / lpr);
     const int64_t rq = (n + 64 / lpr - 1) / (64 / lpr);
-    const int64_t max_waves = (int64_t)cu_count * kGemvWaves * gemv1_waves_per_simd(gpl);
+    const int64_t max_waves = (int64_t)cu_count * kGemvWaves * gemv1_wps(gpl, rq, cu_count);
     const int64_t per = (rq + max_waves - 1) / max_waves;
     const int64_t waves = (rq + per - 1) / per;
     return (waves + kGemvWaves - 1) / kGemvWaves;            // one list per workgroup
