@@ -589,6 +589,36 @@ def test_gemv_topk_selects_from_the_gemv_logits(q4, orc, m, n, k, topk):
         assert_valid_topk(rws[i], y_ref[i], bound[i], "token %d" % i)
 
 
+@pytest.mark.parametrize("k", [512, 1024])
+@pytest.mark.parametrize("delta", [-4, 0, 4])
+def test_gemv1_second_wave_threshold(q4, orc, k, delta):
+    """m = 1 at k <= 1024 runs a second wave per SIMD only when every wave gets two
+    4-row steps or more, i.e. from 16 x CUs steps (n = 64 x CUs rows) on: rows on both
+    sides of that switch (the grid, and so the number of top-k lists, changes there).
+    Products against the oracle, the top-k selection against q4_gemv's logits and
+    the oracle's products, and a two-matrix q4_gemv_multi whose rows together cross
+    the switch, bit-identical to q4_gemv alone."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    n = 64 * cu + delta
+    x, packed, scales, y_ref, bound = _case(orc, 1, n, k, seed=n + k)
+    xg, pg, sg = gpu(x), gpu(packed), gpu(scales.view(np.float16))
+    _log("q4_gemv / q4_gemv_topk m=1 n=%d k=%d (%d CUs)" % (n, k, cu))
+    y = q4.q4_gemv(xg, pg, sg)
+    values, rows = q4.q4_gemv_topk(xg, pg, sg, 20)
+    torch.cuda.synchronize()
+    lg = y.cpu().numpy()
+    assert_within(lg.astype(np.float64), y_ref, bound, "q4_gemv")
+    want = select_topk(lg[0], 20)
+    assert np.array_equal(rows.cpu().numpy()[0], want)
+    assert np.array_equal(values.cpu().numpy()[0].view(np.uint32), lg[0][want].view(np.uint32))
+    assert_valid_topk(rows.cpu().numpy()[0], y_ref[0], bound[0], "topk")
+    half = n // 2
+    mats = [(pg[:half], sg[:half]), (pg[half:], sg[half:])]
+    ys = q4.q4_gemv_multi(xg, mats)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], y[:, :half]) and torch.equal(ys[1], y[:, half:])
+
+
 @pytest.mark.parametrize("m,n", [(1, 300), (1, 5000), (3, 5000)])
 def test_gemv_topk_ties(q4, orc, m, n):
     """Equal logits rank by row.  5000 equal rows exceed the candidate buffer
