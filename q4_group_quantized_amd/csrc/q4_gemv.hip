@@ -214,9 +214,9 @@ struct FlatSegments {
     const uint8_t* packed[kFlatMaxSegments];
     const uint16_t* scales[kFlatMaxSegments];
     float* y[kFlatMaxSegments];
-    int64_t n[kFlatMaxSegments];
-    int64_t w0[kFlatMaxSegments];
-    int64_t wn[kFlatMaxSegments];
+    int32_t n[kFlatMaxSegments];                 // rows (< 2^31)
+    int32_t w0[kFlatMaxSegments];                // first wave
+    int32_t wn[kFlatMaxSegments];                // waves
     int count;
 };
 static_assert(kFlatMaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MULTI_MAX matrices");
@@ -231,19 +231,19 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
     const int lr = lane >> 4, lj = lane & 15;             // code loads
     const int sr = lane >> 2, sp = lane & 3;              // scale loads
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t w = (int64_t)blockIdx.x * kGemvWaves + wave;
+    const int w = (int)blockIdx.x * kGemvWaves + wave;
     // this wave's matrix (wave-uniform selects over constant indices)
     const uint8_t* __restrict__ packed = seg.packed[0];
     const uint16_t* __restrict__ scales = seg.scales[0];
     float* __restrict__ y = seg.y[0];
-    int64_t N = seg.n[0], w0 = seg.w0[0], W = seg.wn[0];
+    int N = seg.n[0], w0 = seg.w0[0], W = seg.wn[0];
 #pragma unroll
     for (int i = 1; i < kFlatMaxSegments; ++i)
         if (i < seg.count && w >= seg.w0[i]) {
             packed = seg.packed[i]; scales = seg.scales[i]; y = seg.y[i];
             N = seg.n[i]; w0 = seg.w0[i]; W = seg.wn[i];
         }
-    const int64_t RB = (N + 15) / 16;
+    const int64_t RB = ((int64_t)N + 15) / 16;
     const int64_t lw = w - w0;                           // >= W: a spare wave, no rows
     const int64_t base = RB / W, extra = RB % W;
     const int64_t rb_begin = lw < W ? lw * base + (lw < extra ? lw : extra) : RB;
@@ -261,23 +261,32 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
     // flight instead of waiting for every load at each step.  Steps past the
     // wave's range re-read row N-1; groups past G re-read group G-1 (their
     // activations in LDS are zero).
+    //
+    // Addressing: the row block's first row is wave-uniform (scalar
+    // registers); a lane adds a 32-bit offset inside the block (row < 16,
+    // K/2 <= 2^23 bytes per row), so the only per-lane work is clamping rows
+    // past N in the matrix's last block.  Steps past the wave's range re-read
+    // its last row block.
     const int64_t rb_end = rb_begin + count;
+    const int64_t rb_last = (rb_end > 0 ? rb_end : 1) - 1;
     int64_t lrb = rb_begin;
     int lt = 0;
     auto load_next = [&]() -> Step {
         Step st;
+        const int64_t lb = lrb < rb_end ? lrb : rb_last;             // uniform
+        const int64_t left = N - lb * 16;                            // rows from lb on, >= 1
+        const int rmax = (int)(left < 16 ? left : 16) - 1;           // last real row in the block
+        const uint8_t* pblk = packed + lb * 16 * (int64_t)(K / 2);
+        const uint16_t* sblk = scales + lb * 16 * (int64_t)G;
         const int g = lt * kStepGroups + lj;
-        const int gc = g < G ? g : G - 1;
+        const uint32_t gofs = 16u * (uint32_t)(g < G ? g : G - 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t n = lrb * 16 + 4 * i + lr;
-            const int64_t nc = (lrb < rb_end && n < N) ? n : N - 1;
-            st.v[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t*>(packed + nc * (int64_t)(K / 2) + 16 * gc));
+            const int r = 4 * i + lr;
+            const uint32_t ofs = (uint32_t)(r < rmax ? r : rmax) * (uint32_t)(K / 2) + gofs;
+            st.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pblk + ofs));
         }
-        const int64_t ns = lrb * 16 + sr;
-        const int64_t nsc = (lrb < rb_end && ns < N) ? ns : N - 1;
-        const uint16_t* srow = scales + nsc * (int64_t)G;
+        const uint16_t* srow = sblk + (uint32_t)(sr < rmax ? sr : rmax) * (uint32_t)G;
         const int gs = lt * kStepGroups + 4 * sp;
         if (kWhole16) {                   // G % 16 == 0 (whole step), 8-byte aligned scales
             const uint2 v = *reinterpret_cast<const uint2*>(srow + gs);
@@ -476,15 +485,15 @@ hipError_t launch_gemv_t(const uint16_t* x, int m, int k, int count,
             seg.packed[s] = packed[s];
             seg.scales[s] = scales[s];
             seg.y[s] = y[s];
-            seg.n[s] = n[s];
-            seg.w0[s] = waves;
-            seg.wn[s] = (rb + per - 1) / per;
+            seg.n[s] = (int32_t)n[s];                    // n < 2^31 (checked by the API)
+            seg.w0[s] = (int32_t)waves;
+            seg.wn[s] = (int32_t)((rb + per - 1) / per);
             waves += seg.wn[s];
             whole = whole && (reinterpret_cast<uintptr_t>(scales[s]) & 7) == 0;
         }
         if (count == 1) {
             // one matrix: every wave of the grid takes a share
-            seg.wn[0] = (waves + kGemvWaves - 1) / kGemvWaves * kGemvWaves;
+            seg.wn[0] = (int32_t)((waves + kGemvWaves - 1) / kGemvWaves * kGemvWaves);
         }
         const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
         const void* fn = whole ? reinterpret_cast<const void*>(&gemv_flat_kernel<TB, true>)
