@@ -926,3 +926,88 @@ def test_workload_full_size(q4, orc, key, idx):
     assert np.array_equal(gp, rp), "codes differ from the oracle's"
     y_ref, bound = orc.matmul(x, rp, rs)
     assert_within(gy.astype(np.float64), y_ref, bound, "%s %s" % (key, mat.name))
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture: every entry point replayed from a graph
+# --------------------------------------------------------------------------
+
+def test_graph_replay_matches_eager(q4):
+    """Every entry point captured once into a HIP graph (after eager calls, which also
+    set the kernels' LDS attributes) and the graph replayed three times, with the outputs
+    cleared and unrelated eager work and synchronizations between replays: every replay
+    gives the eager results bit for bit (the kernels take no memset, and the top-k paths
+    clear their own counters)."""
+    rng = np.random.default_rng(2024)
+    w1 = gpu((rng.standard_normal((4099, 2560)) * 0.02).astype(np.float32))
+    w2 = gpu((rng.standard_normal((700, 1024)) * 0.02).astype(np.float32))
+    wf = gpu((rng.standard_normal((1000, 1024)) * 0.02).astype(np.float16))
+    x1 = gpu(rng.standard_normal((1, 2560)).astype(np.float16))
+    x8 = gpu(rng.standard_normal((8, 2560)).astype(np.float16))
+    x40 = gpu(rng.standard_normal((40, 1024)).astype(np.float16))
+    x3 = gpu(rng.standard_normal((3, 1024)).astype(np.float16))
+    p1, s1 = q4.q4_quantize(w1)
+    p2, s2 = q4.q4_quantize(w2)
+    torch.cuda.synchronize()
+    outs = {
+        "quantize": (torch.empty_like(p1), torch.empty_like(s1)),
+        "gemv1": torch.empty((1, 4099), device=DEV),
+        "gemv8": torch.empty((8, 4099), device=DEV),
+        "multi1": [torch.empty((1, 4099), device=DEV), torch.empty((1, 2000), device=DEV)],
+        "multi3": [torch.empty((3, 700), device=DEV), torch.empty((3, 300), device=DEV)],
+        "gemm": torch.empty((40, 700), device=DEV),
+        "gemm_multi": [torch.empty((40, 700), device=DEV), torch.empty((40, 300), device=DEV)],
+        "topk1": (torch.empty((1, 20), device=DEV), torch.empty((1, 20), dtype=torch.int32, device=DEV)),
+        "topk8": (torch.empty((8, 5), device=DEV), torch.empty((8, 5), dtype=torch.int32, device=DEV)),
+        "noalloc": (torch.empty((1, 20), device=DEV), torch.empty((1, 20), dtype=torch.int32, device=DEV)),
+        "gemv_f16": torch.empty((3, 1000), device=DEV),
+        "gemm_f16": torch.empty((40, 1000), device=DEV),
+    }
+    ws1 = torch.empty(q4.q4_gemv_topk_workspace_size(1, 4099, 2560) + 256, dtype=torch.uint8, device=DEV)
+    ws8 = torch.empty(q4.q4_gemv_topk_workspace_size(8, 4099, 2560) + 256, dtype=torch.uint8, device=DEV)
+
+    def calls():
+        q4.q4_quantize(w1, out=outs["quantize"])
+        q4.q4_gemv(x1, p1, s1, out=outs["gemv1"])
+        q4.q4_gemv(x8, p1, s1, out=outs["gemv8"])
+        q4.q4_gemv_multi(x1, [(p1, s1), (p1[:2000], s1[:2000])], out=outs["multi1"])
+        q4.q4_gemv_multi(x3, [(p2, s2), (p2[:300], s2[:300])], out=outs["multi3"])
+        q4.q4_gemm(x40, p2, s2, out=outs["gemm"])
+        q4.q4_gemm_multi(x40, [(p2, s2), (p2[:300], s2[:300])], out=outs["gemm_multi"])
+        q4.q4_gemv_topk(x1, p1, s1, 20, workspace=ws1, out=outs["topk1"])
+        q4.q4_gemv_topk(x8, p1, s1, 5, workspace=ws8, out=outs["topk8"])
+        q4.q4_gemv_topk_noalloc(x1, p1, s1, 20, out=outs["noalloc"])
+        q4.q4_gemv_f16(x3, wf, out=outs["gemv_f16"])
+        q4.q4_gemm_f16(x40, wf, out=outs["gemm_f16"])
+
+    def flat():
+        res = []
+        for v in outs.values():
+            res.extend(v if isinstance(v, (list, tuple)) else [v])
+        return res
+
+    _log("graph capture of every entry point")
+    calls()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in flat()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    scratch = torch.empty((8, 4099), device=DEV)
+    for replay in range(3):
+        for t in flat():
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(flat(), eager)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                "replay %d: output %d differs from the eager call" % (replay, i)
+        q4.q4_gemv(x8, p1, s1, out=scratch)            # unrelated eager work in between
+        torch.cuda.synchronize()
