@@ -457,6 +457,8 @@ struct G32 {
     static_assert(NAW <= 16 && NCW <= 16 && NSW <= 16, "load offsets fit one u32x16_t");
     static_assert(S >= 2, "at least double buffering");
     static_assert(kLds <= 160 * 1024, "LDS of one CU");
+    // a stage issues the next stage's loads after its second block
+    static_assert(MB * NB >= 2, "at least two 32x32 blocks per wave");
 };
 
 template <int MB, int NB, int WN, int WK, int KG, int S, bool SV, bool TAIL>
@@ -844,14 +846,15 @@ hipError_t launch_gemm32_t(const uint16_t* x, int count, const uint8_t* const* p
 }
 
 // Tile shapes for m > 32, largest first, with the time one full round of
-// them takes (k = 2560, n = 4096, one tile per CU; measured on MI355X over
-// m = 128 ... 2048: the 32 x 32 block kernel from m = 384 on, the 16 x 16
-// block tiles below).
+// them takes (k = 2560, n = 4096, one tile per CU, measured on MI355X: m =
+// 1024, 512, 256 and 128 respectively).  All four are 32 x 32 block tiles; the
+// two smaller ones replaced 16 x 16 block tiles of the same sizes (m = 256:
+// 16.5 -> 12.4 us, m = 128: 12.5 -> 11.3 us).
 constexpr TileChoice kTiles[] = {
     {128, 128, 35.f},      // gemm32_kernel<4, 1, 4, 2, 4, 3>: 4 column slices x 2 K phases
-    {64, 128, 20.f},       // gemm32_kernel<2, 2, 2, 4, 8, 2>: 2 column slices x 4 K phases
-    {64, 64, 16.f},        // gemm_kernel<64, 2, 4, 2, 2>
-    {32, 64, 15.f},        // gemm_kernel<32, 2, 4, 2, 2>
+    {64, 128, 19.f},       // gemm32_kernel<2, 2, 2, 4, 8, 2>: 2 column slices x 4 K phases
+    {64, 64, 12.5f},       // gemm32_kernel<2, 1, 2, 4, 8, 3>: 2 column slices x 4 K phases
+    {32, 64, 11.3f},       // gemm32_kernel<1, 2, 1, 4, 8, 3>: 1 column slice x 4 K phases
 };
 
 hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* const* packed,
@@ -867,8 +870,8 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
     switch (choose_tile(kTiles, 4, m, count, n, device_info(dev).cu_count)) {
         case 0: return launch_gemm32_t<4, 1, 4, 2, 4, 3>(x, count, packed, scales, y, n, m, k, stream);
         case 1: return launch_gemm32_t<2, 2, 2, 4, 8, 2>(x, count, packed, scales, y, n, m, k, stream);
-        case 2: return launch_gemm_t<64, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
-        default: return launch_gemm_t<32, 2, 4, 2, 2>(x, count, packed, scales, y, n, m, k, stream);
+        case 2: return launch_gemm32_t<2, 1, 2, 4, 8, 3>(x, count, packed, scales, y, n, m, k, stream);
+        default: return launch_gemm32_t<1, 2, 1, 4, 8, 3>(x, count, packed, scales, y, n, m, k, stream);
     }
 }
 
