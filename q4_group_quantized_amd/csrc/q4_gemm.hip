@@ -6,11 +6,18 @@
 // format of their quantization sections (symmetric, group size 32, 16-entry
 // table dequantization).
 //
-// Arithmetic.  For every 32-element group j, one v_mfma_f32_16x16x32_f16 per
-// 16x16 output block multiplies fp16 activations by the group's exact fp16
-// levels -8..7 (K = 32 is exactly one group) into a fresh accumulator P, and
-// the group's scale is applied in fp32 afterwards: acc += s[n, j] * P.  In the
-// 16x16 D layout a lane's four values share one column, hence one scale.
+// Two kernels.  m <= 32 runs gemm_kernel below (16 x 16 output blocks,
+// 16- or 32-row tiles of 16 columns, so a small batch still spreads its
+// weight traffic over every CU); m > 32 runs gemm32_kernel further down
+// (32 x 32 output blocks, tiles of 32 x 64 up to 128 x 128 chosen per launch).
+// Both apply each group's scale in fp32 after that group's own MFMA.
+//
+// Arithmetic (gemm_kernel).  For every 32-element group j, one
+// v_mfma_f32_16x16x32_f16 per 16x16 output block multiplies fp16 activations by
+// the group's exact fp16 levels -8..7 (K = 32 is exactly one group) into a
+// fresh accumulator P, and the group's scale is applied in fp32 afterwards:
+// acc += s[n, j] * P.  In the 16x16 D layout a lane's four values share one
+// column, hence one scale.
 //
 // Work split.  A workgroup (4, 8 or 16 waves: one, two or four per SIMD) owns a
 // BM x (16*NB*WN) tile of y (WN = 1, 2 or 4 column slices of NB = 1 or 2
@@ -19,9 +26,10 @@
 // unpacked by
 // exactly one wave and every activation is read from LDS by WN waves.  The
 // WK partial tiles are added in LDS at the end in a fixed order
-// (deterministic).  The tile shape is chosen per launch from m and the number
-// of tiles of all its matrices (choose_tile); the order of the fp32 sums, and
-// so the last bits of a result, depend on that shape.
+// (deterministic).  The tile shape (for m > 32, gemm32_kernel's) is chosen
+// per launch from m and the number of tiles of all its matrices
+// (choose_tile); the order of the fp32 sums, and so the last bits of a
+// result, depend on that shape.
 //
 // Data movement.  Every operand goes straight from global memory into LDS
 // with direct-to-LDS loads, through an S-stage ring per K slice:
