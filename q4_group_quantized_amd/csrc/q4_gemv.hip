@@ -725,10 +725,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
         if (lane < kTopkList) cand[wave][lane] = list;
         __syncthreads();
         if (wave == 0) {
-            const uint64_t b1 = lane < kTopkList ? cand[1][lane] : cand[2][lane - kTopkList];
-            list = topk_merge_batch(list, b1, lane);
-            const uint64_t b2 = lane < kTopkList ? cand[3][lane] : 0;
-            list = topk_merge_batch(list, b2, lane);
+            // the other lists are sorted already: three bitonic merges
+            // (6 stages each) instead of sorting them as batches (~27 each)
+#pragma unroll
+            for (int v = 1; v < kGemvWaves; ++v)
+                list = topk_merge_sorted(list, cand[v][lane & (kTopkList - 1)], lane);
             if (lane < kTopkList) partials[(int64_t)blockIdx.x * kTopkList + lane] = list;
         }
     }

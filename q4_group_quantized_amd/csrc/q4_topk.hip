@@ -4,7 +4,7 @@
 // m = 1 (greedy decoding, top-k sampling: QORA-LLM-0.8B model card, CLI
 // options and "Sampling Defaults"): the streaming GEMV itself keeps each
 // wave's top-32 (gemv1_kernel<..., TOPK>), so the 248,320 logits never leave
-// the chip; merge_kernel below reduces the per-wave lists.  m = 2..8 (the
+// the chip; merge_kernel below reduces the per-workgroup lists.  m = 2..8 (the
 // verify batch of speculative decoding: Rai article, speculative decoding
 // section): the product is written to the workspace, scan_kernel turns every
 // slice of a token's logits into a top-32 list, and merge_kernel reduces them.
@@ -20,110 +20,165 @@ constexpr int kScanWaves = 4;
 constexpr int kScanLists = kScanBlocks * kScanWaves;
 constexpr int kMergeWaves = 16;
 
+constexpr int kScanDepth = 8;          // batches of 64 logits loaded at once
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Token t = blockIdx.x / kScanBlocks; wave v of the token's kScanLists waves
 // takes logits [v * slice, (v + 1) * slice) and writes its list to
-// partials[(t * lists + v) * 32 ..].
+// partials[(t * lists + v) * 32 ..].  Only keys above the running list's last
+// entry (0 until it holds 32) can enter it: those are appended to a wave
+// buffer in LDS and merged 64 at a time.  Over a slice of s logits about
+// 32 ln(s / 32) keys ever pass (the i-th one seen enters the running top 32
+// with probability 32 / i), so most batches of 64 cost a compare and a ballot
+// instead of a 64-key sort (one sort per batch took 23.5 us for 8 x 248,320
+// logits).
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(const float* __restrict__ logits,
                                                                int64_t n, int64_t lists,
                                                                uint64_t* __restrict__ partials) {
+    __shared__ uint64_t buf_s[kScanWaves][128];
     const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint64_t* buf = buf_s[wave];
     const int64_t t = blockIdx.x / kScanBlocks;
-    const int64_t v = (blockIdx.x % kScanBlocks) * kScanWaves +
-                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t v = (blockIdx.x % kScanBlocks) * kScanWaves + wave;
     const int64_t slice = (n + kScanLists - 1) / kScanLists;
     const int64_t beg = v * slice;
     const int64_t end = beg + slice < n ? beg + slice : n;
     const float* row = logits + t * n;
-    uint64_t list = 0;
-    for (int64_t i = beg; i < end; i += 64) {
-        const int64_t j = i + lane;
-        const uint64_t key = j < end ? topk_key(row[j], (uint32_t)j) : 0;
-        list = topk_merge_batch(list, key, lane);
+    uint64_t list = 0, last = 0;
+    uint32_t filled = 0;                          // keys in the buffer (wave-uniform)
+    for (int64_t i0 = beg; i0 < end; i0 += 64 * kScanDepth) {
+        float val[kScanDepth];
+#pragma unroll
+        for (int d = 0; d < kScanDepth; ++d) {
+            const int64_t j = i0 + 64 * d + lane;
+            val[d] = j < end ? row[j] : 0.f;
+        }
+#pragma unroll
+        for (int d = 0; d < kScanDepth; ++d) {
+            const int64_t j = i0 + 64 * d + lane;
+            const uint64_t key = j < end ? topk_key(val[d], (uint32_t)j) : 0;
+            const bool pass = key > last;
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(pass);
+            if (bal == 0) continue;
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (pass) buf[filled + below] = key;
+            filled += (uint32_t)__builtin_popcountll(bal);
+            if (filled >= 64) {
+                __builtin_amdgcn_wave_barrier();
+                const uint64_t batch = buf[lane];
+                const uint64_t rest = buf[64 + lane];
+                __builtin_amdgcn_wave_barrier();
+                list = topk_merge_batch(list, batch, lane);
+                last = readlane64(list, kTopkList - 1);
+                filled -= 64;
+                if ((uint32_t)lane < filled) buf[lane] = rest;
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
     }
+    __builtin_amdgcn_wave_barrier();
+    if (filled > 0) list = topk_merge_batch(list, (uint32_t)lane < filled ? buf[lane] : 0, lane);
     if (lane < kTopkList) partials[(t * lists + v) * kTopkList + lane] = list;
 }
 
-// Merges two sorted lists held in lanes 0..31 of `a` and of `b` (descending)
-// into the top 32 of their union, in lanes 0..31 of the result.
-__device__ __forceinline__ uint64_t merge_sorted(uint64_t a, uint64_t b, int lane) {
-    const uint32_t src = (uint32_t)(63 - lane) * 4u;
-    const uint32_t rlo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)src, (int)(uint32_t)b);
-    const uint32_t rhi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)src, (int)(uint32_t)(b >> 32));
-    uint64_t v = lane < kTopkList ? a : (((uint64_t)rhi << 32) | rlo);
-    v = cmpx<32>(v, (lane & 32) == 0);
-    v = cmpx<16>(v, (lane & 16) == 0);
-    v = cmpx<8>(v, (lane & 8) == 0);
-    v = cmpx<4>(v, (lane & 4) == 0);
-    v = cmpx<2>(v, (lane & 2) == 0);
-    v = cmpx<1>(v, (lane & 1) == 0);
-    return v;
-}
-
 constexpr int kCandCap = 2048;
-constexpr int kCandBatch = 8;         // keys per thread loaded before testing
+constexpr int kHeadCap = 64 * kMergeWaves;   // list heads kept in LDS
+constexpr int kSelCap = 1024;                // lists whose entries are read
+
+// Appends the passing lanes' items through one LDS counter per wave: `store`
+// gets each passing lane's slot.  `pass` may differ between lanes; the call
+// must be made by every lane of the wave.
+template <typename Store>
+__device__ __forceinline__ void wave_append(bool pass, uint32_t* counter, int lane, Store store) {
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(pass);
+    if (bal == 0) return;
+    const int first = (int)__builtin_ctzll(bal);
+    uint32_t base = 0;
+    if (lane == first) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(bal));
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (pass) store(base + below);
+}
 
 // One workgroup per token over its lists partials[t * lists .. + lists), each
 // sorted descending.
-//  1. The lists' first entries (their maxima) are reduced to their top 32;
-//     entry topk-1 of that, T, is a key at most the topk-th largest of all,
-//     since the topk heads above it are distinct entries.
-//  2. Every entry >= T is a candidate (collected in LDS; their order is
-//     irrelevant) -- typically little more than topk of them.
+//  1. Bound: lane l of wave 0 takes the largest head (first entry) of lists
+//     l, l + 64, ...; entry topk-1 of those 64 maxima sorted, T, is at most
+//     the topk-th largest key overall (topk distinct keys reach it).
+//  2. Only a list whose head reaches T can hold a key >= T: those lists
+//     (typically about topk of them) are collected, and their entries >= T
+//     are the candidates.
 //  3. Wave 0 reduces the candidates to the sorted top 32 and writes topk.
-// If more than kCandCap entries reach T (many equal logits), every list is
-// merged instead.  Both routes give the top-k of the same set: the result is
-// unique.
+// Only the heads and the selected lists are read -- reading every list's 32
+// entries into one workgroup was bound by that CU's load bandwidth (7.5 against
+// 4.3 us on 501 lists).  If more than kSelCap lists or kCandCap entries reach
+// T (many equal logits), every list is merged instead.  Both routes give the
+// top-k of the same set: the result is unique.
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
     const uint64_t* __restrict__ partials, int64_t lists, int topk, float* __restrict__ values,
     int32_t* __restrict__ rows) {
     __shared__ uint64_t wave_lists[kMergeWaves][kTopkList];
+    __shared__ uint64_t heads[kHeadCap];
+    __shared__ uint32_t sel[kSelCap];
     __shared__ uint64_t cand[kCandCap];
-    __shared__ uint32_t ncand;
+    __shared__ uint32_t nsel, ncand;
+    __shared__ uint64_t thr_s;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int64_t t = blockIdx.x;
     const uint64_t* src = partials + t * lists * kTopkList;
-    if (threadIdx.x == 0) ncand = 0;
-
-    // 1. heads: wave wv takes lists wv*64 + lane (+ 1024 j), sorted into its top 32
-    uint64_t heads = 0;
-    for (int64_t l0 = 64 * wv; l0 < lists; l0 += 64 * kMergeWaves) {
-        const int64_t l = l0 + lane;
-        heads = topk_merge_batch(heads, l < lists ? src[l * kTopkList] : 0, lane);
+    if (threadIdx.x == 0) {
+        nsel = 0;
+        ncand = 0;
     }
-    if (lane < kTopkList) wave_lists[wv][lane] = heads;
+    const int64_t hl = lists < kHeadCap ? lists : kHeadCap;
+    auto head = [&](int64_t l) { return l < kHeadCap ? heads[l] : src[l * kTopkList]; };
+    if ((int64_t)threadIdx.x < hl) heads[threadIdx.x] = src[(int64_t)threadIdx.x * kTopkList];
     __syncthreads();
-#pragma unroll 1
-    for (int half = kMergeWaves / 2; half > 0; half >>= 1) {      // tree over the waves
-        if (wv < half) {
-            const uint64_t b = wave_lists[wv + half][lane & 31];
-            heads = merge_sorted(heads, b, lane);
-        }
-        __syncthreads();
-        if (wv < half && lane < kTopkList) wave_lists[wv][lane] = heads;
-        __syncthreads();
-    }
-    const uint64_t thr = wave_lists[0][topk - 1];
 
-    // 2. candidates: each thread loads kCandBatch keys before testing any of
-    // them, so their global loads are in flight together (one load per
-    // iteration waited for every key in turn: ~16 round trips at m = 1)
-    const int64_t total = lists * kTopkList;
-    constexpr int64_t kStride = 64 * kMergeWaves;
-    for (int64_t i0 = threadIdx.x; i0 < total; i0 += kStride * kCandBatch) {
-        uint64_t keys[kCandBatch];
-#pragma unroll
-        for (int b = 0; b < kCandBatch; ++b) {
-            const int64_t i = i0 + b * kStride;
-            keys[b] = i < total ? src[i] : 0;
+    // 1. the bound T
+    if (wv == 0) {
+        uint64_t hm = 0;
+        for (int64_t l = lane; l < lists; l += 64) {
+            const uint64_t h = head(l);
+            hm = h > hm ? h : hm;
         }
-#pragma unroll
-        for (int b = 0; b < kCandBatch; ++b) {
-            if (keys[b] >= thr && keys[b] != 0) {
-                const uint32_t pos = atomicAdd(&ncand, 1u);
-                if (pos < kCandCap) cand[pos] = keys[b];
-            }
+        hm = wave_sort_desc(hm, lane);
+        const uint64_t thr = readlane64(hm, topk - 1);
+        if (lane == 0) thr_s = thr;
+    }
+    __syncthreads();
+    const uint64_t thr = thr_s;
+
+    // 2. lists whose head reaches T, then their entries that do
+    for (int64_t l0 = 0; l0 < lists; l0 += 64 * kMergeWaves) {
+        const int64_t l = l0 + threadIdx.x;
+        const uint64_t h = l < lists ? head(l) : 0;
+        wave_append(h >= thr && h != 0, &nsel, lane, [&](uint32_t pos) {
+            if (pos < kSelCap) sel[pos] = (uint32_t)l;
+        });
+    }
+    __syncthreads();
+    const uint32_t ns = nsel;
+    if (ns <= kSelCap) {
+        for (uint32_t j0 = 0; j0 < ns * kTopkList; j0 += 64 * kMergeWaves) {
+            const uint32_t j = j0 + threadIdx.x;
+            const uint64_t key =
+                j < ns * kTopkList ? src[(int64_t)sel[j / kTopkList] * kTopkList + j % kTopkList] : 0;
+            wave_append(key >= thr && key != 0, &ncand, lane, [&](uint32_t pos) {
+                if (pos < kCandCap) cand[pos] = key;
+            });
         }
+    } else if (threadIdx.x == 0) {
+        ncand = kCandCap + 1;
     }
     __syncthreads();
     const uint32_t nc = ncand;
@@ -142,13 +197,13 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
         // then a tree over the waves)
         uint64_t list = 0;
         for (int64_t l = wv; l < lists; l += kMergeWaves)
-            list = merge_sorted(list, src[l * kTopkList + (lane & 31)], lane);
+            list = topk_merge_sorted(list, src[l * kTopkList + (lane & 31)], lane);
         __syncthreads();
         if (lane < kTopkList) wave_lists[wv][lane] = list;
         __syncthreads();
 #pragma unroll 1
         for (int half = kMergeWaves / 2; half > 0; half >>= 1) {
-            if (wv < half) list = merge_sorted(list, wave_lists[wv + half][lane & 31], lane);
+            if (wv < half) list = topk_merge_sorted(list, wave_lists[wv + half][lane & 31], lane);
             __syncthreads();
             if (wv < half && lane < kTopkList) wave_lists[wv][lane] = list;
             __syncthreads();

@@ -104,6 +104,23 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key, int lane) {
     return key;
 }
 
+// Merges two sorted lists held in lanes 0..31 of `a` and of `b` (descending)
+// into the top 32 of their union, in lanes 0..31 of the result: b reversed
+// behind a is one bitonic sequence, so six exchange stages sort it.
+__device__ __forceinline__ uint64_t topk_merge_sorted(uint64_t a, uint64_t b, int lane) {
+    const uint32_t src = (uint32_t)(63 - lane) * 4u;
+    const uint32_t rlo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)src, (int)(uint32_t)b);
+    const uint32_t rhi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)src, (int)(uint32_t)(b >> 32));
+    uint64_t v = lane < kTopkList ? a : (((uint64_t)rhi << 32) | rlo);
+    v = cmpx<32>(v, (lane & 32) == 0);
+    v = cmpx<16>(v, (lane & 16) == 0);
+    v = cmpx<8>(v, (lane & 8) == 0);
+    v = cmpx<4>(v, (lane & 4) == 0);
+    v = cmpx<2>(v, (lane & 2) == 0);
+    v = cmpx<1>(v, (lane & 1) == 0);
+    return v;
+}
+
 // Merges a batch of 64 keys (any order, one per lane) into the running list
 // (lanes 0..31, sorted descending); returns the new list in lanes 0..31.  A
 // batch with no key above the list's last entry cannot change the list and is
@@ -114,20 +131,8 @@ __device__ __forceinline__ uint64_t topk_merge_batch(uint64_t list, uint64_t bat
         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(list >> 32), kTopkList - 1);
     const uint64_t last = ((uint64_t)last_hi << 32) | last_lo;
     if (__builtin_amdgcn_ballot_w64(batch > last) == 0) return list;
-    batch = wave_sort_desc(batch, lane);
-    // lanes 32..63 take the batch's top 32 in ascending order: with the list
-    // (descending) in lanes 0..31 that is one bitonic sequence
-    const uint32_t src = (uint32_t)(63 - lane) * 4u;
-    const uint32_t rlo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)src, (int)(uint32_t)batch);
-    const uint32_t rhi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)src, (int)(uint32_t)(batch >> 32));
-    uint64_t v = lane < kTopkList ? list : (((uint64_t)rhi << 32) | rlo);
-    v = cmpx<32>(v, (lane & 32) == 0);
-    v = cmpx<16>(v, (lane & 16) == 0);
-    v = cmpx<8>(v, (lane & 8) == 0);
-    v = cmpx<4>(v, (lane & 4) == 0);
-    v = cmpx<2>(v, (lane & 2) == 0);
-    v = cmpx<1>(v, (lane & 1) == 0);
-    return v;
+    // the batch's top 32, sorted, merged like a list
+    return topk_merge_sorted(list, wave_sort_desc(batch, lane), lane);
 }
 
 }  // namespace q4
