@@ -170,10 +170,10 @@ TILING_CASES = [(64, 1000, 256), (256, 4096, 256), (384, 4096, 128), (512, 4096,
 @pytest.mark.parametrize("m,n,k", TILING_CASES, ids=["m%d-n%d-k%d" % c for c in TILING_CASES])
 def test_prefill_every_tile_shape(q4, orc, m, n, k):
     """Shapes for which the GEMM picks each of its tile shapes on a 256-CU
-    device, compared in full: 32x64 and 64x64 (16x16 blocks); 64x128 (32x32
-    blocks) with a group count that is and is not a multiple of its 8-group
-    stage; 128x128 (32x32 blocks) with and without a partial last stage, with
-    ragged rows and columns, and with n % 4 != 0 (element-wise stores)."""
+    device, compared in full: 32x64 (16-group stages, here one partial stage)
+    and 64x64; 64x128 with a group count that is and is not a multiple of its
+    8-group stage; 128x128 with and without a partial last stage, with ragged
+    rows and columns, and with n % 4 != 0 (element-wise stores)."""
     x, packed, scales, y_ref, bound = _case(orc, m, n, k, seed=m + n + k)
     _log("q4_gemm m=%d n=%d k=%d" % (m, n, k))
     y = product(q4, "q4_gemm", x, packed, scales)
