@@ -89,8 +89,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(const float* __re
 }
 
 constexpr int kCandCap = 2048;
-constexpr int kHeadCap = 64 * kMergeWaves;   // list heads kept in LDS
-constexpr int kSelCap = 1024;                // lists whose entries are read
+constexpr int kHeadCap = 64 * kMergeWaves;   // lists per token at most (heads kept in LDS)
 
 // Appends the passing lanes' items through one LDS counter per wave: `store`
 // gets each passing lane's slot.  `pass` may differ between lanes; the call
@@ -119,15 +118,15 @@ __device__ __forceinline__ void wave_append(bool pass, uint32_t* counter, int la
 //  3. Wave 0 reduces the candidates to the sorted top 32 and writes topk.
 // Only the heads and the selected lists are read -- reading every list's 32
 // entries into one workgroup was bound by that CU's load bandwidth (7.5 against
-// 4.3 us on 501 lists).  If more than kSelCap lists or kCandCap entries reach
-// T (many equal logits), every list is merged instead.  Both routes give the
+// 4.3 us on 501 lists).  If more than kCandCap entries reach T (many equal
+// logits), every list is merged instead.  Both routes give the
 // top-k of the same set: the result is unique.
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
     const uint64_t* __restrict__ partials, int64_t lists, int topk, float* __restrict__ values,
     int32_t* __restrict__ rows) {
     __shared__ uint64_t wave_lists[kMergeWaves][kTopkList];
     __shared__ uint64_t heads[kHeadCap];
-    __shared__ uint32_t sel[kSelCap];
+    __shared__ uint32_t sel[kHeadCap];
     __shared__ uint64_t cand[kCandCap];
     __shared__ uint32_t nsel, ncand;
     __shared__ uint64_t thr_s;
@@ -139,18 +138,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
         nsel = 0;
         ncand = 0;
     }
-    const int64_t hl = lists < kHeadCap ? lists : kHeadCap;
-    auto head = [&](int64_t l) { return l < kHeadCap ? heads[l] : src[l * kTopkList]; };
-    if ((int64_t)threadIdx.x < hl) heads[threadIdx.x] = src[(int64_t)threadIdx.x * kTopkList];
+    // lists <= kHeadCap (launch_gemv_topk): one head per thread
+    if ((int64_t)threadIdx.x < lists) heads[threadIdx.x] = src[(int64_t)threadIdx.x * kTopkList];
     __syncthreads();
 
     // 1. the bound T
     if (wv == 0) {
         uint64_t hm = 0;
-        for (int64_t l = lane; l < lists; l += 64) {
-            const uint64_t h = head(l);
-            hm = h > hm ? h : hm;
-        }
+        for (int64_t l = lane; l < lists; l += 64) hm = heads[l] > hm ? heads[l] : hm;
         hm = wave_sort_desc(hm, lane);
         const uint64_t thr = readlane64(hm, topk - 1);
         if (lane == 0) thr_s = thr;
@@ -159,26 +154,20 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
     const uint64_t thr = thr_s;
 
     // 2. lists whose head reaches T, then their entries that do
-    for (int64_t l0 = 0; l0 < lists; l0 += 64 * kMergeWaves) {
-        const int64_t l = l0 + threadIdx.x;
-        const uint64_t h = l < lists ? head(l) : 0;
-        wave_append(h >= thr && h != 0, &nsel, lane, [&](uint32_t pos) {
-            if (pos < kSelCap) sel[pos] = (uint32_t)l;
-        });
+    {
+        const int64_t l = threadIdx.x;
+        const uint64_t h = l < lists ? heads[l] : 0;
+        wave_append(h >= thr && h != 0, &nsel, lane, [&](uint32_t pos) { sel[pos] = (uint32_t)l; });
     }
     __syncthreads();
-    const uint32_t ns = nsel;
-    if (ns <= kSelCap) {
-        for (uint32_t j0 = 0; j0 < ns * kTopkList; j0 += 64 * kMergeWaves) {
-            const uint32_t j = j0 + threadIdx.x;
-            const uint64_t key =
-                j < ns * kTopkList ? src[(int64_t)sel[j / kTopkList] * kTopkList + j % kTopkList] : 0;
-            wave_append(key >= thr && key != 0, &ncand, lane, [&](uint32_t pos) {
-                if (pos < kCandCap) cand[pos] = key;
-            });
-        }
-    } else if (threadIdx.x == 0) {
-        ncand = kCandCap + 1;
+    const uint32_t ns = nsel;                     // <= lists
+    for (uint32_t j0 = 0; j0 < ns * kTopkList; j0 += 64 * kMergeWaves) {
+        const uint32_t j = j0 + threadIdx.x;
+        const uint64_t key =
+            j < ns * kTopkList ? src[(int64_t)sel[j / kTopkList] * kTopkList + j % kTopkList] : 0;
+        wave_append(key >= thr && key != 0, &ncand, lane, [&](uint32_t pos) {
+            if (pos < kCandCap) cand[pos] = key;
+        });
     }
     __syncthreads();
     const uint32_t nc = ncand;
@@ -218,12 +207,22 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Lists of the streaming m = 1 GEMV's top-k form (one per workgroup), or 0
+// where it does not apply (m > 1, k outside that kernel, or more workgroups
+// than the merge kernel keeps heads for: then the product, scan and merge
+// route serves the call, with kScanLists lists per token).
+int64_t fused_topk_lists(int64_t m, int64_t n, int64_t k, int cu_count) {
+    const int64_t lists = m == 1 ? gemv1_topk_lists(n, k, cu_count) : 0;
+    return lists <= kHeadCap ? lists : 0;
+}
+static_assert(kScanLists <= kHeadCap, "the merge kernel keeps every list head in LDS");
+
 }  // namespace
 
 // Workspace: [partial lists: m * lists * 32 keys][logits: m * n fp32, m > 1 or
 // k outside the streaming kernel only].
 size_t gemv_topk_workspace(int64_t m, int64_t n, int64_t k, int cu_count) {
-    const int64_t fused = m == 1 ? gemv1_topk_lists(n, k, cu_count) : 0;
+    const int64_t fused = fused_topk_lists(m, n, k, cu_count);
     const int64_t lists = fused > 0 ? fused : kScanLists;
     size_t bytes = align_up((size_t)(m * lists * kTopkList) * sizeof(uint64_t));
     if (fused == 0) bytes += align_up((size_t)(m * n) * sizeof(float));
@@ -238,7 +237,7 @@ hipError_t launch_gemv_topk(const uint16_t* x, const uint8_t* packed, const uint
     if (e != hipSuccess) return e;
     const int cu = device_info(dev).cu_count;
     uint64_t* partials = static_cast<uint64_t*>(workspace);
-    const int64_t fused = m == 1 ? gemv1_topk_lists(n, k, cu) : 0;
+    const int64_t fused = fused_topk_lists(m, n, k, cu);
     int64_t lists;
     if (fused > 0) {
         lists = fused;
