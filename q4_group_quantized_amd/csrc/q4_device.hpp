@@ -158,6 +158,11 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// s_waitcnt operand that waits for this wave's LDS operations only (lgkmcnt
+// 0; vmcnt and expcnt at their maxima): gfx9 encoding, vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8.
+constexpr int kLdsStoresDone = 0xC07F;
+
 // Workgroup barrier that leaves outstanding global loads in flight
 // (__syncthreads() also fences memory, which drains every pending load).
 // The signal fences only stop the compiler from moving memory accesses across

@@ -621,7 +621,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
     }
     const int64_t lw = w - wave0;
     const bool active = lw < waves;
-    if (!TOPK && !active) return;           // the top-k variant's idle waves join the final merge
     const int64_t q0 = lw * base + (lw < extra ? lw : extra);
     const int64_t cnt = active ? base + (lw < extra ? 1 : 0) : 0;
     const int64_t row0 = RPS * q0 + r;
@@ -663,10 +662,40 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
             rs[slot][i] = sp[LPR * i];
         }
     };
-    if (cnt > 0) {
+    // Activations: the workgroup stages x in LDS once -- every thread loads
+    // at most kXPT of its 16-byte chunks, issued before the weight loads so
+    // that waiting for them leaves those in flight -- and each lane reads its
+    // GPL groups from there.  Loading them per lane from global memory, four
+    // rows of lanes fetching the same values, cost ~3 us per 4B decode step
+    // in the small projection launches.  Chunk c of group g sits at slot
+    // 5 g + c: one 16-byte pad per group spreads the 16 groups that a read
+    // touches over the LDS banks.
+    constexpr int kXChunks = 4 * LPR * GPL;                  // K / 8
+    constexpr int kXPT = (kXChunks + kGemvThreads - 1) / kGemvThreads;
+    // (every x load and store is unconditional -- threads past the last chunk
+    // re-load it and store to spare slots -- so that no branch lets the
+    // compiler move the loads behind the weight loads, which made it wait
+    // for all of them and shortened the loop's prefetch)
+    __shared__ u32x4_t xs[kXPT * kGemvThreads / 4 * 5];
+    u32x4_t xv[kXPT];
 #pragma unroll
-        for (int p = 0; p < PF; ++p) load(p, p);
+    for (int t = 0; t < kXPT; ++t) {
+        const int j = (int)threadIdx.x + kGemvThreads * t;
+        xv[t] = *reinterpret_cast<const u32x4_t*>(x + 8 * (j < kXChunks ? j : kXChunks - 1));
     }
+    __builtin_amdgcn_sched_barrier(0);      // keep them ahead of the weight loads
+    // an idle wave (cnt = 0, past its segment's waves: q0 >= 1) loads rows
+    // row0 - RPS (clamped to n - 1) that it never uses
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load(p, p);
+#pragma unroll
+    for (int t = 0; t < kXPT; ++t) {
+        const int j = (int)threadIdx.x + kGemvThreads * t;
+        xs[j / 4 * 5 + j % 4] = xv[t];
+    }
+    __builtin_amdgcn_s_waitcnt(kLdsStoresDone);
+    barrier_keep_loads();
+    if (!TOPK && !active) return;           // the top-k variant's idle waves join the final merge
 
     // this lane's activations, as fp16 pairs in unpack order
     uint32_t xr[GPL][16];
@@ -674,11 +703,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
     for (int i = 0; i < GPL; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const u32x4_t v = permute_x8(*reinterpret_cast<const u32x4_t*>(
-                x + 32 * (sub + LPR * i) + 8 * c));
+            const u32x4_t v = permute_x8(xs[(sub + LPR * i) * 5 + c]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) xr[i][4 * c + e] = v[e];
         }
+    // Enter the loop with the first PF steps landed: with them still in
+    // flight the compiler's wait at the loop head kept only ~3 loads
+    // outstanding in every later step (4B head 54.8 -> 63.6 us).
+    __builtin_amdgcn_s_waitcnt(0);
 
     const uint32_t mask = kc.mask, mask16 = kc.mask16;
     const uint32_t magic = to_vgpr(kc.magic);
