@@ -458,7 +458,9 @@ def decode_set(torch, q4, lib, workload, warmup, steps, side_steps):
     set_bytes = sum(p.bytes for p in prods)
     per = []
     for p in prods:
-        t = time_launches(torch, lib, "q4_gemv", p, max(100, 4 * copies), sh)
+        # replayed from a graph: eager launches of the small matrices would
+        # measure the host's launch rate, not the kernel
+        t = graph_rate(torch, lib, "q4_gemv", p, 4 * copies, 10)
         per.append({"matrix": p.mat.name, "n": p.mat.n, "k": p.mat.k, "us": round(t * 1e6, 3),
                     "GB_s": round(p.bytes / t / 1e9, 1),
                     "hbm_frac": round(p.bytes / t / 1e9 / HBM_PEAK_GBS, 4)})

@@ -540,6 +540,7 @@ hipError_t launch_gemv_t(const uint16_t* x, int m, int k, int count,
 // ---------------------------------------------------------------------------
 
 constexpr int kGemv1MaxGpl = 8;                 // groups per lane
+constexpr int kGemv1DeferRows = 256;            // rows of a wave's deferred results
 
 // Sum over aligned groups of LPR lanes (8, 16 or 32); every lane of the group
 // receives the total.
@@ -588,12 +589,20 @@ static_assert(kGemv1MaxSegments == Q4_MULTI_MAX, "segment table must hold Q4_MUL
 // the compiler keeps PF steps outstanding instead of draining the queue; the
 // last PF steps are computed after the loop without new loads.
 //
+// DEFER: each step's results go to a wave-private LDS buffer instead of to y,
+// and the wave writes its whole range (RPS * cnt consecutive rows) with
+// coalesced 4-byte stores after its last step.  A global store inside the
+// pipelined loop shares the in-order vmcnt queue with the loads, so every
+// later wait for a step's codes also waits for the store's write-back; with
+// the stores after the loop the queue holds loads only.  The host selects
+// DEFER when every wave's range fits the buffer (kGemv1DeferRows rows).
+//
 // TOPK: instead of storing y, every wave keeps the 32 largest (logit, row)
 // keys of its rows (q4_topk.hpp): each step's RPS results go to a 64-entry
 // wave buffer in LDS, merged into the running list whenever it is full; at
 // the end the four lists of a workgroup are merged and written to
 // partials[blockIdx.x * 32 .. +32) (idle waves contribute empty lists).
-template <int LPR, int GPL, int PF, bool TOPK>
+template <int LPR, int GPL, int PF, bool TOPK, bool DEFER>
 __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
     const uint16_t* __restrict__ x, int K, Gemv1Segments seg, SpliceConsts kc,
     uint64_t* __restrict__ partials) {
@@ -628,6 +637,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
     // top-k state: running list (lanes 0..31) and this wave's candidate buffer
     __shared__ uint64_t cand[TOPK ? kGemvWaves : 1][64];
     uint64_t* buf = cand[TOPK ? (threadIdx.x >> 6) : 0];
+    // deferred results of this wave's rows (DEFER)
+    __shared__ float ydef[DEFER ? kGemvWaves : 1][DEFER ? kGemv1DeferRows : 1];
+    float* ybuf = ydef[DEFER ? (threadIdx.x >> 6) : 0];
     uint64_t list = 0;
     int filled = 0;                                   // steps in the buffer
     auto flush = [&]() {
@@ -643,6 +655,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
         if (TOPK) {
             if (sub == 0) buf[filled * RPS + r] = row < N ? topk_key(acc, (uint32_t)row) : 0;
             if (++filled == 64 / RPS) flush();
+        } else if (DEFER) {
+            if (sub == 0) ybuf[RPS * f + r] = acc;
         } else {
             if (sub == 0 && row < N) y[row] = acc;
         }
@@ -750,6 +764,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
             emit(acc, f0 + p);
         }
     }
+    if constexpr (DEFER) {
+        // rows RPS * q0 + i, i < RPS * cnt, are this wave's range, in order;
+        // LDS serves one wave's accesses in issue order, so the reads see
+        // every write above
+        __builtin_amdgcn_wave_barrier();
+        const int rows = (int)(RPS * cnt);
+        for (int i = lane; i < rows; i += 64) {
+            const int64_t row = RPS * q0 + i;
+            if (row < N) y[row] = ybuf[i];
+        }
+    }
     if constexpr (TOPK) {
         // the workgroup's four lists -> one, in partials[blockIdx.x * 32 ..)
         if (filled > 0) flush();
@@ -841,12 +866,25 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
         wave0 += waves;
     }
     const int blocks = (int)((wave0 + kGemvWaves - 1) / kGemvWaves);
+    // Results wait in LDS until a wave's last step (DEFER) when every wave's
+    // range fits the buffer and the launch runs two waves per SIMD (GPL <= 3):
+    // bit-identical either way; 0.8B LM head (k = 1024) 24.8 -> 24.2 us,
+    // while at k = 2560 (one wave per SIMD, two steps in flight) the 4B LM
+    // head and its decode step ran 0.2-0.8 us slower with it.
+    int64_t most = 0;
+    for (int s = 0; s < count; ++s) {
+        const int64_t c = seg.base[s] + (seg.extra[s] > 0 ? 1 : 0);
+        most = c > most ? c : most;
+    }
     if (partials)
-        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, true>), dim3(blocks), dim3(kGemvThreads),
-                           0, stream, x, k, seg, kSpliceConsts, partials);
+        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, true, false>), dim3(blocks),
+                           dim3(kGemvThreads), 0, stream, x, k, seg, kSpliceConsts, partials);
+    else if (gemv1_waves_per_simd(GPL) > 1 && most * RPS <= kGemv1DeferRows)
+        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, false, true>), dim3(blocks),
+                           dim3(kGemvThreads), 0, stream, x, k, seg, kSpliceConsts, partials);
     else
-        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, false>), dim3(blocks), dim3(kGemvThreads),
-                           0, stream, x, k, seg, kSpliceConsts, partials);
+        hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, false, false>), dim3(blocks),
+                           dim3(kGemvThreads), 0, stream, x, k, seg, kSpliceConsts, partials);
     return hipGetLastError();
 }
 
