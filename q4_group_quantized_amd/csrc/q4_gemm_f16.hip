@@ -7,12 +7,16 @@
 // table; GPU prefill section), i.e. the F16 GEMV of the QORA-LLM-0.8B model
 // card ("AVX-512 SIMD Acceleration", F16 GEMV row) for a whole token batch.
 //
-// Arithmetic.  fp16 weights are the B operand of v_mfma_f32_16x16x32_f16 as
-// they stand, activations the A operand; every product of two fp16 values is
-// exact and each 16x16 output block accumulates in fp32 over all of K in the
-// matrix core itself -- no dequantization and no per-group scale.
+// Arithmetic.  fp16 weights are the B operand of the MFMA as they stand,
+// activations the A operand; every product of two fp16 values is exact and
+// each output block accumulates in fp32 over all of K in the matrix core
+// itself -- no dequantization and no per-group scale.
 //
-// Work split and data movement follow the Q4 GEMM: a workgroup owns a
+// Two kernels: m <= 32 runs gemm_f16_kernel (16 x 16 blocks,
+// v_mfma_f32_16x16x32_f16, described next); m > 32 runs gemm32_f16_kernel
+// further down (32 x 32 blocks, whole-row staging of both operands).
+//
+// gemm_f16_kernel.  Work split and data movement follow the Q4 GEMM: a workgroup owns a
 // BM x (32*WN) tile of y; its waves are WN column slices of 32 x WK slices of
 // K; every operand goes straight from global memory into LDS with
 // direct-to-LDS loads through an S-stage ring, 16 rows x 64 bytes (one
@@ -250,6 +254,283 @@ hipError_t launch_gemm_f16_t(const uint16_t* x, const uint16_t* w, float* y, int
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// m > 32: 32 x 32 output blocks (v_mfma_f32_32x32x16_f16)
+//
+// Both operands are rows of fp16 with K contiguous (x[m][t], w[n][t]), so
+// they are staged alike: a stage holds KG consecutive 32-wide K steps
+// ("groups") of the tile's BM activation rows followed by its BN weight rows,
+// each row's KG * 64 bytes contiguous in LDS.  Every wave instruction loads
+// whole row slices (64 / (4 KG) rows x 64 KG bytes, i.e. 4 rows x 256 bytes
+// at KG = 4) straight into LDS; the 16-byte chunk c of stage row r sits at
+// position c ^ (r & 7) of its row, so that the operand reads of a wave touch
+// distinct banks.  The MFMAs accumulate over all of K in place: no
+// dequantization and no per-group scale, so the loop issues no VALU work.
+//
+// Work split.  WM x WN x WK waves: wave (wm, wn, wk) computes the 32 MB x
+// 32 NB block of y at rows 32 MB wm, columns 32 NB wn, over the groups wk,
+// wk + WK, ... of every stage.  The WK partial tiles are added in LDS in a
+// fixed order (deterministic for a given m, n, k).
+// K mapping inside a group: lane (i, g) (i = lane % 32, g = lane / 32) feeds
+// MFMA h (h = 0, 1) with the 8 elements of chunk 2g + h, of activation row i
+// and of weight row i alike.
+// ---------------------------------------------------------------------------
+typedef float f16x32_acc_t __attribute__((ext_vector_type(16)));
+typedef uint32_t f16x32_u32x16_t __attribute__((ext_vector_type(16)));
+
+template <int MB, int NB, int WM, int WN, int WK, int KG, int S>
+struct F16x32 {
+    static constexpr int BM = 32 * MB * WM;
+    static constexpr int BN = 32 * NB * WN;
+    static constexpr int W = WM * WN * WK;
+    static constexpr int kThreads = 64 * W;
+    static constexpr int GPW = KG / WK;                  // groups per wave and stage
+    static constexpr int kRowBytes = KG * 64;            // one row's slice of a stage
+    static constexpr int kABytes = BM * kRowBytes;
+    static constexpr int kStage = (BM + BN) * kRowBytes;
+    static constexpr int NL = kStage / 1024;             // load instructions per stage
+    static constexpr int NLW = NL / W;                   // ... per wave
+    static constexpr int RS = BN + 4;                    // floats per row of a partial tile
+    static constexpr int kRedBytes = WK * BM * RS * 4;
+    static constexpr int kLds = S * kStage > kRedBytes ? S * kStage : kRedBytes;
+    static constexpr int CPR = 4 * KG;                   // 16-byte chunks per stage row
+    static constexpr int RPI = 64 / CPR;                 // stage rows per load instruction
+    static_assert(KG % WK == 0, "whole groups per wave");
+    static_assert(KG == 2 || KG == 4 || KG == 8 || KG == 16, "power-of-two stage");
+    static_assert(NL % W == 0, "equal loads per wave");
+    static_assert(NLW <= 16, "load offsets fit one vector");
+    static_assert(BM % RPI == 0, "a load instruction reads one operand only");
+    static_assert(W == 4 || W == 8, "one or two waves per SIMD");
+    static_assert(S >= 2, "at least double buffering");
+    static_assert(kLds <= 160 * 1024, "LDS of one CU");
+};
+
+template <int MB, int NB, int WM, int WN, int WK, int KG, int S, bool TAIL>
+__global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm32_f16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ y,
+    int M, int64_t N, int K, int G, int64_t tiles_n, int64_t tile_base, int vec_store) {
+    using C = F16x32<MB, NB, WM, WN, WK, KG, S>;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int64_t tile = tile_base + blockIdx.x;
+    const int64_t n0 = (tile % tiles_n) * C::BN;
+    const int64_t m0 = (tile / tiles_n) * C::BM;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave % WM, wn = (wave / WM) % WN, wk = wave / (WM * WN);
+    const int li = lane & 31, lg = lane >> 5;
+    const int nstages = (G + KG - 1) / KG;
+
+    // ---- per-lane load offsets: instruction t of this wave reads stage rows
+    // RPI q .. RPI q + RPI - 1 (q = wave * NLW + t), activation rows below BM,
+    // weight rows from BM on; rows past M or N are clamped to the last one ----
+    f16x32_u32x16_t off = {};
+    uint32_t isw = 0;                                   // bit t: instruction t reads weights
+    int grp[C::NLW];                                    // group of the stage each lane loads
+#pragma unroll
+    for (int t = 0; t < C::NLW; ++t) {
+        const int q = wave * C::NLW + t;
+        const int r = q * C::RPI + lane / C::CPR;
+        const int c = (lane % C::CPR) ^ (r & 7);
+        int64_t row;
+        if (q * C::RPI < C::BM) {
+            row = min<int64_t>(m0 + r, M - 1) - m0;
+        } else {
+            row = min<int64_t>(n0 + (r - C::BM), N - 1) - n0;
+            isw |= 1u << t;
+        }
+        grp[t] = c >> 2;
+        off[t] = (uint32_t)(row * K * 2) + (uint32_t)(c * 16);
+    }
+    const unsigned char* xbase = reinterpret_cast<const unsigned char*>(x + m0 * K);
+    const unsigned char* wbase = reinterpret_cast<const unsigned char*>(w + n0 * K);
+
+    // Loads of stage st into ring buffer buf.  With TAIL (G not a multiple of
+    // KG), groups past G in the last stage re-read group G - 1 (in bounds;
+    // their products are never computed).
+    auto issue = [&](int st, int buf) {
+        unsigned char* sb = smem + buf * C::kStage;
+        const int g0 = st * KG;
+        const int over = g0 - (G - 1);
+#pragma unroll
+        for (int t = 0; t < C::NLW; ++t) {
+            const uint32_t back = TAIL ? (uint32_t)max(0, over + grp[t]) * 64u : 0u;
+            const unsigned char* base = ((isw >> t) & 1u) ? wbase : xbase;
+            __builtin_amdgcn_global_load_lds(base + (size_t)g0 * 64 + (off[t] - back),
+                                             (lds_void_t*)(sb + (wave * C::NLW + t) * 1024),
+                                             16, 0, 0);
+        }
+    };
+
+    // ---- per-lane operand offsets inside a stage ----
+    int rA[C::GPW][2], rB[C::GPW][2];
+#pragma unroll
+    for (int u = 0; u < C::GPW; ++u) {
+        const int gl = wk + WK * u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int pos = ((gl * 4 + 2 * lg + h) ^ (li & 7)) * 16;
+            rA[u][h] = (32 * MB * wm + li) * C::kRowBytes + pos;
+            rB[u][h] = C::kABytes + (32 * NB * wn + li) * C::kRowBytes + pos;
+        }
+    }
+
+    f16x32_acc_t acc[MB][NB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rb][nb][v] = 0.f;
+
+    struct Ops {
+        half8_t a[MB][2];
+        half8_t b[NB][2];
+    };
+    auto read_ops = [&](Ops& o, const unsigned char* sb, int u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+                o.a[rb][h] = *reinterpret_cast<const half8_t*>(sb + rA[u][h] +
+                                                               rb * 32 * C::kRowBytes);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                o.b[nb][h] = *reinterpret_cast<const half8_t*>(sb + rB[u][h] +
+                                                               nb * 32 * C::kRowBytes);
+        }
+    };
+    auto mfmas = [&](const Ops& o) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[rb][h], o.b[nb][h],
+                                                                         acc[rb][nb], 0, 0, 0);
+    };
+    // every wave's groups of one stage, operands read one group ahead
+    auto stage = [&](const unsigned char* sb) {
+        Ops ops[2];
+        read_ops(ops[0], sb, 0);
+#pragma unroll
+        for (int u = 0; u < C::GPW; ++u) {
+            if (u + 1 < C::GPW) read_ops(ops[(u + 1) & 1], sb, u + 1);
+            mfmas(ops[u & 1]);
+        }
+    };
+
+    // Every iteration issues one stage's loads (stages past the end re-load
+    // the last one into a buffer nobody reads again), so stage st has landed
+    // once at most S - 2 later stages' loads remain in flight; after the
+    // barrier every wave's loads of it have landed, and every wave is done
+    // with the buffer that the refill overwrites.
+    auto wait_stage = [&]() {
+        __builtin_amdgcn_s_waitcnt(f16_vmcnt_imm(C::NLW * (S - 2)));
+        barrier_keep_loads();
+    };
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u) issue(min(u, nstages - 1), u);
+
+    const int nfull = G / KG;
+    int st = 0;
+    for (; st + S <= nfull; st += S) {
+#pragma unroll
+        for (int b = 0; b < S; ++b) {
+            wait_stage();
+            issue(min(st + b + S - 1, nstages - 1), (b + S - 1) % S);
+            stage(smem + b * C::kStage);
+        }
+    }
+    for (; st < nfull; ++st) {
+        const int b = st % S;
+        wait_stage();
+        issue(min(st + S - 1, nstages - 1), (b + S - 1) % S);
+        stage(smem + b * C::kStage);
+    }
+    if (TAIL && nfull < nstages) {          // the partial last stage: its real groups only
+        const int b = nfull % S;
+        wait_stage();
+        const unsigned char* sb = smem + b * C::kStage;
+#pragma unroll
+        for (int u = 0; u < C::GPW; ++u)
+            if (nfull * KG + wk + WK * u < G) {
+                Ops o;
+                read_ops(o, sb, u);
+                mfmas(o);
+            }
+    }
+
+    // ---- add the WK partial tiles (fixed order) and store ----
+    __builtin_amdgcn_s_waitcnt(f16_vmcnt_imm(0));
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    {
+        float* dst = red + wk * C::BM * C::RS + (32 * MB * wm) * C::RS + 32 * NB * wn + li;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    dst[(32 * rb + 8 * (v >> 2) + 4 * lg + (v & 3)) * C::RS + 32 * nb] =
+                        acc[rb][nb][v];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < C::BM * C::BN / 4; i += C::kThreads) {
+        const int r = i / (C::BN / 4), c = 4 * (i % (C::BN / 4));
+        const int64_t m = m0 + r, n = n0 + c;
+        if (m >= M) continue;
+        f32x4_t t = *reinterpret_cast<const f32x4_t*>(red + r * C::RS + c);
+#pragma unroll
+        for (int q = 1; q < WK; ++q)
+            t += *reinterpret_cast<const f32x4_t*>(red + q * C::BM * C::RS + r * C::RS + c);
+        float* out = y + m * N + n;
+        if (vec_store && n + 3 < N) {
+            *reinterpret_cast<f32x4_t*>(out) = t;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) out[e] = t[e];
+        }
+    }
+}
+
+template <int MB, int NB, int WM, int WN, int WK, int KG, int S, bool TAIL>
+hipError_t launch_gemm32_f16_grid(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
+                                  int64_t n, int64_t k, int vec, hipStream_t stream) {
+    using C = F16x32<MB, NB, WM, WN, WK, KG, S>;
+    const int64_t tiles_n = (n + C::BN - 1) / C::BN;
+    const int64_t tiles = tiles_n * ((m + C::BM - 1) / C::BM);
+    static std::atomic<uint64_t> lds_done{0};
+    hipError_t e = allow_dynamic_lds(
+        reinterpret_cast<const void*>(&gemm32_f16_kernel<MB, NB, WM, WN, WK, KG, S, TAIL>),
+        C::kLds, lds_done);
+    if (e != hipSuccess) return e;
+    for (int64_t base = 0; base < tiles; base += kGemmF16MaxGrid) {
+        const int64_t grid = tiles - base < kGemmF16MaxGrid ? tiles - base : kGemmF16MaxGrid;
+        hipLaunchKernelGGL((gemm32_f16_kernel<MB, NB, WM, WN, WK, KG, S, TAIL>),
+                           dim3((unsigned)grid), dim3(C::kThreads), C::kLds, stream, x, w, y,
+                           (int)m, n, (int)k, (int)(k / 32), tiles_n, base, vec);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int MB, int NB, int WM, int WN, int WK, int KG, int S>
+hipError_t launch_gemm32_f16_t(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
+                               int64_t n, int64_t k, hipStream_t stream) {
+    // 16-byte stores when every output row is 16-byte aligned
+    const int vec = (reinterpret_cast<uintptr_t>(y) % 16) == 0 && n % 4 == 0;
+    if ((k / 32) % KG != 0)
+        return launch_gemm32_f16_grid<MB, NB, WM, WN, WK, KG, S, true>(x, w, y, m, n, k, vec,
+                                                                       stream);
+    return launch_gemm32_f16_grid<MB, NB, WM, WN, WK, KG, S, false>(x, w, y, m, n, k, vec,
+                                                                    stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_f16(const uint16_t* x, const uint16_t* w, float* y, int64_t m,
@@ -257,24 +538,28 @@ hipError_t launch_gemm_f16(const uint16_t* x, const uint16_t* w, float* y, int64
     if (m <= 8) return launch_gemv_f16(x, w, y, m, n, k, stream);
     if (m <= 16) return launch_gemm_f16_t<16, 1, 4, 2, 4>(x, w, y, m, n, k, stream);
     if (m <= 32) return launch_gemm_f16_t<32, 1, 4, 2, 4>(x, w, y, m, n, k, stream);
-    // above, the tile shape with the least estimated time (choose_tile); the
-    // 128- and 64-column-wide shapes without a K split pay with 3.6x the weight
-    // bytes of Q4 (fewer weight re-reads per output).  Round times measured
-    // at k = 2560, n = 4096, one tile per CU.
+    // above, the 32 x 32 block kernel with the tile shape of least estimated
+    // time (choose_tile).  Round times: one tile per CU, k = 2560, n = 4096,
+    // measured on MI355X at m = 1024, 512, 256 and 128; they follow the
+    // operand bytes a tile moves from L2 into LDS, (BM + BN) * k * 2, at
+    // ~45-55 GB/s per CU.  For the 128 x 128 tile, 2-group stages in a
+    // four-stage ring beat 4-group stages in two (m = 2048: 56.4-57.5 ->
+    // 53.0-53.4 us); the other shapes were swept over ring depths of 2-6 and
+    // 32 x 32 to 64 x 64 wave blocks without a gain.
     static constexpr TileChoice kTilesF16[] = {
-        {128, 128, 38.5f},     // gemm_f16_kernel<128, 4, 1, 1, 8>
-        {64, 128, 23.6f},      // gemm_f16_kernel<64, 4, 1, 2, 4>
-        {64, 64, 19.6f},       // gemm_f16_kernel<64, 2, 4, 2, 2>
-        {32, 64, 16.2f},       // gemm_f16_kernel<32, 2, 4, 2, 2>
+        {128, 128, 27.7f},     // gemm32_f16_kernel<2, 2, 2, 2, 2, 2, 4>: 2 x 2 quadrants x 2 K phases
+        {64, 128, 17.5f},      // gemm32_f16_kernel<2, 2, 1, 2, 4, 4, 3>: 2 column slices x 4 K phases
+        {64, 64, 11.3f},       // gemm32_f16_kernel<2, 1, 1, 2, 4, 4, 4>
+        {32, 64, 9.1f},        // gemm32_f16_kernel<1, 1, 1, 2, 4, 8, 3>
     };
     int dev = 0;
     const hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     switch (choose_tile(kTilesF16, 4, m, 1, &n, device_info(dev).cu_count)) {
-        case 0: return launch_gemm_f16_t<128, 4, 1, 1, 8>(x, w, y, m, n, k, stream);
-        case 1: return launch_gemm_f16_t<64, 4, 1, 2, 4>(x, w, y, m, n, k, stream);
-        case 2: return launch_gemm_f16_t<64, 2, 4, 2, 2>(x, w, y, m, n, k, stream);
-        default: return launch_gemm_f16_t<32, 2, 4, 2, 2>(x, w, y, m, n, k, stream);
+        case 0: return launch_gemm32_f16_t<2, 2, 2, 2, 2, 2, 4>(x, w, y, m, n, k, stream);
+        case 1: return launch_gemm32_f16_t<2, 2, 1, 2, 4, 4, 3>(x, w, y, m, n, k, stream);
+        case 2: return launch_gemm32_f16_t<2, 1, 1, 2, 4, 4, 4>(x, w, y, m, n, k, stream);
+        default: return launch_gemm32_f16_t<1, 1, 1, 2, 4, 8, 3>(x, w, y, m, n, k, stream);
     }
 }
 

@@ -723,7 +723,8 @@ def test_gemv_f16_product(q4, orc, m, n, k):
                   "q4_gemv_f16 m=%d n=%d k=%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("fn,m", [("q4_gemv_f16", 1), ("q4_gemv_f16", 8), ("q4_gemm_f16", 9)])
+@pytest.mark.parametrize("fn,m", [("q4_gemv_f16", 1), ("q4_gemv_f16", 8), ("q4_gemm_f16", 9),
+                                  ("q4_gemm_f16", 33)])
 def test_f16_longest_k(q4, orc, fn, m):
     """fp16 weights at the largest k the contract allows (2^24), n = 3."""
     n, k = 3, 2 ** 24
@@ -815,16 +816,19 @@ def test_gemm_f16_product(q4, orc, m, n, k):
                   "q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
 
 
-F16_TILING_CASES = [(64, 1000, 256), (256, 4096, 256), (384, 4096, 128), (768, 4100, 96),
-                    (1030, 4100, 96)]
+F16_TILING_CASES = [(64, 1000, 256), (100, 1000, 96), (256, 4096, 256), (250, 4090, 160),
+                    (384, 4096, 128), (380, 4100, 96), (1030, 4096, 256), (768, 4100, 96),
+                    (1000, 4000, 288), (2000, 4096, 64)]
 
 
 @pytest.mark.parametrize("m,n,k", F16_TILING_CASES,
                          ids=["m%d-n%d-k%d" % c for c in F16_TILING_CASES])
 def test_gemm_f16_every_tile_shape(q4, orc, m, n, k):
-    """Shapes for which the fp16-weight GEMM picks each of its tile shapes on a
-    256-CU device (32x64, 64x64, 64x128, 128x128, and 64x128 with ragged rows
-    and columns), compared in full."""
+    """Shapes for which the fp16-weight GEMM picks each of its m > 32 tile
+    shapes on a 256-CU device (32x64, 64x64, 64x128 and 128x128), each once
+    with whole stages and once with a partial last stage (k / 32 not a
+    multiple of the stage's groups) and ragged rows and columns, compared in
+    full."""
     x, w = _f16_case(m, n, k, seed=m + n + k)
     _log("q4_gemm_f16 m=%d n=%d k=%d" % (m, n, k))
     y = q4.q4_gemm_f16(gpu(x), gpu(w))
