@@ -174,6 +174,14 @@ __device__ __forceinline__ void barrier_keep_loads() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Buffer resources for raw (untyped, byte-addressed) buffer loads: word 3 of
+// a gfx9 descriptor with a non-zero data format (32-bit) and no swizzle or
+// thread-id addressing, and the cache-policy operand that marks a load
+// non-temporal (printed as "nt").  A raw buffer load at an offset at or past
+// the descriptor's byte count returns zero without touching memory.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kBufferNontemporal = 2;
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

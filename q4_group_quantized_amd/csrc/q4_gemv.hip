@@ -262,40 +262,50 @@ __device__ __forceinline__ void gemv_flat(const uint16_t* __restrict__ x,
     // wave's range re-read row N-1; groups past G re-read group G-1 (their
     // activations in LDS are zero).
     //
-    // Addressing: the row block's first row is wave-uniform (scalar
-    // registers); a lane adds a 32-bit offset inside the block (row < 16,
-    // K/2 <= 2^23 bytes per row), so the only per-lane work is clamping rows
-    // past N in the matrix's last block.  Steps past the wave's range re-read
+    // Addressing: buffer loads from the row block's first row.  The block's
+    // base and byte count are wave-uniform (scalar registers, rebuilt per
+    // step); a lane adds a fixed 32-bit offset inside the block (row < 16,
+    // K/2 <= 2^23 bytes per row).  Rows past N in the matrix's last block lie
+    // past the buffer's end and read as zeros (their results are never
+    // stored), so no lane clamps a row.  Steps past the wave's range re-read
     // its last row block.
     const int64_t rb_end = rb_begin + count;
     const int64_t rb_last = (rb_end > 0 ? rb_end : 1) - 1;
     int64_t lrb = rb_begin;
     int lt = 0;
+    const int code_lane = lr * (K / 2) + 16 * lj;                // row lr, group lj of a step
+    const int scale_lane = 2 * (sr * G + 4 * sp);                // row sr, groups 4 sp .. +3
     auto load_next = [&]() -> Step {
         Step st;
         const int64_t lb = lrb < rb_end ? lrb : rb_last;             // uniform
         const int64_t left = N - lb * 16;                            // rows from lb on, >= 1
-        const int rmax = (int)(left < 16 ? left : 16) - 1;           // last real row in the block
-        const uint8_t* pblk = packed + lb * 16 * (int64_t)(K / 2);
-        const uint16_t* sblk = scales + lb * 16 * (int64_t)G;
+        const int rows = (int)(left < 16 ? left : 16);
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(packed + lb * 16 * (int64_t)(K / 2)), (short)0, rows * (K / 2), kBufferFlags);
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(scales + lb * 16 * (int64_t)G), (short)0, rows * G * 2, kBufferFlags);
+        // groups past G (last step, G % 16 != 0) re-read group G - 1 of the row
         const int g = lt * kStepGroups + lj;
-        const uint32_t gofs = 16u * (uint32_t)(g < G ? g : G - 1);
+        const int voff = kWhole16 ? code_lane : lr * (K / 2) + 16 * (g < G ? g : G - 1);
+        const int soff = kWhole16 ? 16 * kStepGroups * lt : 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * i + lr;
-            const uint32_t ofs = (uint32_t)(r < rmax ? r : rmax) * (uint32_t)(K / 2) + gofs;
-            st.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pblk + ofs));
-        }
-        const uint16_t* srow = sblk + (uint32_t)(sr < rmax ? sr : rmax) * (uint32_t)G;
+        for (int i = 0; i < 4; ++i)
+            st.v[i] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                             crs, voff, soff + 4 * i * (K / 2), kBufferNontemporal));
         const int gs = lt * kStepGroups + 4 * sp;
         if (kWhole16) {                   // G % 16 == 0 (whole step), 8-byte aligned scales
-            const uint2 v = *reinterpret_cast<const uint2*>(srow + gs);
+            const uint2 v = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(srs, scale_lane,
+                                                            2 * kStepGroups * lt, 0));
             st.s0 = v.x;
             st.s1 = v.y;
         } else {
             uint32_t h[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = srow[min(gs + e, G - 1)];
+            for (int e = 0; e < 4; ++e)
+                h[e] = __builtin_amdgcn_raw_buffer_load_b16(
+                    srs, 2 * (sr * G + (gs + e < G ? gs + e : G - 1)), 0, 0);
             st.s0 = h[0] | (h[1] << 16);
             st.s1 = h[2] | (h[3] << 16);
         }
@@ -662,18 +672,35 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
         }
     };
 
+    // Weight loads are buffer loads from this wave's first row: the wave's
+    // base and the step offset are scalars, the lane's offset within a step
+    // is fixed, so a step costs no vector address arithmetic (the 64-bit
+    // row * stride products it replaced were six quarter-rate VALU
+    // instructions per step).  The buffer ends at the segment's row N: the
+    // lanes of a partial last quad read zeros there, and their results are
+    // never stored.  The host keeps a wave's range below 2 GiB.
+    const int64_t wrow = RPS * q0;
+    const int64_t wrows = N > wrow ? N - wrow : 0;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(packed + wrow * (int64_t)(K / 2)), (short)0,
+        (int)(wrows * (K / 2) < 0x7FFFFFFF ? wrows * (K / 2) : 0x7FFFFFFF), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(scales + wrow * (int64_t)G), (short)0,
+        (int)(wrows * G * 2 < 0x7FFFFFFF ? wrows * G * 2 : 0x7FFFFFFF), kBufferFlags);
+    const int poff = r * (K / 2) + 16 * sub;
+    const int soff = 2 * (r * G + sub);
+    const int last = cnt > 0 ? (int)cnt - 1 : 0;
     u32x4_t rp[PF][GPL];
     uint32_t rs[PF][GPL];
-    auto load = [&](int slot, int64_t f) {
-        int64_t row = row0 + RPS * (f < cnt ? f : cnt - 1);
-        row = row < N ? row : N - 1;            // the segment's last quad may be partial
-        const uint8_t* pp = packed + row * (int64_t)(K / 2) + 16 * sub;
-        const uint16_t* sp = scales + row * (int64_t)G + sub;
+    auto load = [&](int slot, int f) {
+        const int fs = f < last ? f : last;      // past the last step: re-read it
+        const int pstep = fs * (RPS * (K / 2)), sstep = fs * (RPS * G * 2);
 #pragma unroll
         for (int i = 0; i < GPL; ++i) {
-            rp[slot][i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t*>(pp + 16 * LPR * i));
-            rs[slot][i] = sp[LPR * i];
+            rp[slot][i] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, poff + 16 * LPR * i, pstep,
+                                                               kBufferNontemporal));
+            rs[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(srs, soff + 2 * LPR * i, sstep, 0);
         }
     };
     // Activations: the workgroup stages x in LDS once -- every thread loads
@@ -698,8 +725,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
         xv[t] = *reinterpret_cast<const u32x4_t*>(x + 8 * (j < kXChunks ? j : kXChunks - 1));
     }
     __builtin_amdgcn_sched_barrier(0);      // keep them ahead of the weight loads
-    // an idle wave (cnt = 0, past its segment's waves: q0 >= 1) loads rows
-    // row0 - RPS (clamped to n - 1) that it never uses
+    // an idle wave (cnt = 0, past its segment's waves) starts at or past row
+    // N: its buffers are empty and its loads return zeros it never uses
 #pragma unroll
     for (int p = 0; p < PF; ++p) load(p, p);
 #pragma unroll
@@ -721,9 +748,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) xr[i][4 * c + e] = v[e];
         }
+
     // Enter the loop with the first PF steps landed: with them still in
     // flight the compiler's wait at the loop head kept only ~3 loads
-    // outstanding in every later step (4B head 54.8 -> 63.6 us).
+    // outstanding in every later step (4B head 54.8 -> 63.6 us).  Waves of
+    // PF steps or fewer wait here too: skipping the wait for them, so that
+    // each step is computed as soon as it lands, made the 0.8B projection
+    // launches (one step per wave) 0.5 us slower.
     __builtin_amdgcn_s_waitcnt(0);
 
     const uint32_t mask = kc.mask, mask16 = kc.mask16;
@@ -748,8 +779,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
         return lanes_sum<LPR>(acc);
     };
 
-    int64_t f0 = 0;
-    for (; f0 + PF < cnt; f0 += PF) {
+    const int steps = (int)cnt;                 // below 2^31: the host bounds a wave's bytes
+    int f0 = 0;
+    for (; f0 + PF < steps; f0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const float acc = compute(p);
@@ -759,7 +791,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-        if (f0 + p < cnt) {
+        if (f0 + p < steps) {
             const float acc = compute(p);
             emit(acc, f0 + p);
         }
@@ -876,6 +908,10 @@ hipError_t launch_gemv1_t(const uint16_t* x, int k, int count, const uint8_t* co
         const int64_t c = seg.base[s] + (seg.extra[s] > 0 ? 1 : 0);
         most = c > most ? c : most;
     }
+    // a wave addresses its rows with 32-bit buffer offsets: its range must
+    // stay below 2 GiB (with at least one wave per SIMD that takes a matrix
+    // of terabytes, far beyond the device's memory)
+    if ((most + 1) * RPS * (int64_t)(k / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     if (partials)
         hipLaunchKernelGGL((gemv1_kernel<LPR, GPL, PF, true, false>), dim3(blocks),
                            dim3(kGemvThreads), 0, stream, x, k, seg, kSpliceConsts, partials);
