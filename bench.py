@@ -902,6 +902,9 @@ def main() -> int:
     detail["gemm_m2048"] = gemm_case(torch, q4, lib, qi.PREFILL_4B_WIDE, 2048, False, 30)
     log("verify LM head M=8 (wide-scale weights)")
     detail["verify_m8_lm_head"] = gemm_case(torch, q4, lib, qi.LM_HEAD_4B_WIDE, 8, False, 50)
+    log("verify projections M=8 (4B shapes)")
+    detail["verify_m8_projections_4b"] = [gemm_case(torch, q4, lib, mat, 8, False, 60)
+                                          for mat in qi.DECODE_4B[:-1]]
     log("top-k epilogues")
     detail["lm_head_topk20_08b"] = topk_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 20, 100)
     detail["lm_head_argmax_4b_m8"] = topk_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 1, 30)

@@ -107,6 +107,10 @@ q4_status q4_quantize(const float* w, uint8_t* packed, uint16_t* scales,
  * m outside 1..8 -> Q4_ERR_SHAPE (use q4_gemm).
  * Accuracy: fp16 x times exact integers, fp32 accumulation, group scale
  * applied in fp32 after each 32-element dot product.
+ * At m >= 2 a matrix of at most 4096 rows is computed by q4_gemm's
+ * small-batch kernel (16-row tiles; its waves split k), which finishes such
+ * matrices sooner than the streaming GEMV; the kernel, and so the order of
+ * the fp32 sums, depends only on m, n and k.
  */
 q4_status q4_gemv(const uint16_t* x, const uint8_t* packed,
                   const uint16_t* scales, float* y,
@@ -119,9 +123,11 @@ q4_status q4_gemv(const uint16_t* x, const uint8_t* packed,
  * the QORA-LLM-0.8B card ("AVX-512 SIMD Acceleration"), and the q/k/v
  * projections of one layer input in the hybrid DeltaNet/attention stack
  * ("Architecture" table of the same card).  One launch serves the whole set
- * (m = 1..8; at m >= 2 with k above 7680, or 15360 for m <= 4, where the
- * activations no longer fit the LDS at once, one launch per matrix), so the
- * fixed cost of a kernel is paid once, not per matrix.
+ * at m = 1; at m >= 2 one launch serves the matrices of at most 4096 rows
+ * (q4_gemv's small-batch kernel) and one the others (at k above 7680, or
+ * 15360 for m <= 4, where the activations no longer fit the LDS at once, one
+ * launch per matrix), so the fixed cost of a kernel is paid once per kind,
+ * not per matrix.
  *   x       [in]  fp16 bits [m, k], device, 1 <= m <= 8
  *   count         number of matrices, 1 .. Q4_MULTI_MAX
  *   packed  [in]  HOST array of count device pointers, uint8 [n[i], k/2]

@@ -33,6 +33,11 @@
 // 16-byte load when G % 8 == 0 and the scale matrix is 16-byte aligned, else
 // eight 2-byte loads).
 //
+// At m = 2..8 a matrix of at most kGemvTileRows rows is handed to the GEMM's
+// small-batch kernel instead (launch_gemm_small): with one 16-row block per
+// wave walking all of K, a few thousand rows would leave most of the
+// device idle.
+//
 // m = 1 has its own streaming kernel (gemv1_kernel below): there the block-
 // diagonal MFMA would waste 15/16 of the matrix core anyway, and what bounds
 // the kernel is how sequentially each wave walks HBM.  Every wave owns a
@@ -973,6 +978,8 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed,
                        int64_t k, hipStream_t stream) {
     if (m == 1 && gemv1_lanes_per_row(k) != 0)
         return launch_gemv1(x, (int)k, 1, &packed, &scales, &y, &n, nullptr, stream);
+    if (m >= 2 && n <= kGemvTileRows)
+        return launch_gemm_small(x, 1, &packed, &scales, &y, &n, m, k, stream);
     return launch_gemv_blockdiag(x, m, k, 1, &packed, &scales, &y, &n, stream);
 }
 
@@ -1000,7 +1007,33 @@ hipError_t launch_gemv_multi(const uint16_t* x, int64_t m, int64_t k, int count,
                              float* const* y, const int64_t* n, hipStream_t stream) {
     if (m == 1 && gemv1_lanes_per_row(k) != 0)
         return launch_gemv1(x, (int)k, count, packed, scales, y, n, nullptr, stream);
-    return launch_gemv_blockdiag(x, m, k, count, packed, scales, y, n, stream);
+    if (m == 1) return launch_gemv_blockdiag(x, m, k, count, packed, scales, y, n, stream);
+    // m >= 2: every matrix takes the kernel q4_gemv takes for it alone (so
+    // its result is bit-identical): one launch for those of at most
+    // kGemvTileRows rows, one for the rest
+    const uint8_t* sp[kFlatMaxSegments];
+    const uint16_t* ss[kFlatMaxSegments];
+    float* sy[kFlatMaxSegments];
+    int64_t sn[kFlatMaxSegments];
+    const uint8_t* lp[kFlatMaxSegments];
+    const uint16_t* ls[kFlatMaxSegments];
+    float* ly[kFlatMaxSegments];
+    int64_t ln[kFlatMaxSegments];
+    int small = 0, large = 0;
+    for (int s = 0; s < count; ++s) {
+        if (n[s] <= kGemvTileRows) {
+            sp[small] = packed[s]; ss[small] = scales[s]; sy[small] = y[s]; sn[small] = n[s];
+            ++small;
+        } else {
+            lp[large] = packed[s]; ls[large] = scales[s]; ly[large] = y[s]; ln[large] = n[s];
+            ++large;
+        }
+    }
+    if (small > 0) {
+        const hipError_t e = launch_gemm_small(x, small, sp, ss, sy, sn, m, k, stream);
+        if (e != hipSuccess || large == 0) return e;
+    }
+    return launch_gemv_blockdiag(x, m, k, large, lp, ls, ly, ln, stream);
 }
 
 }  // namespace q4

@@ -118,7 +118,10 @@ def test_quantize_midpoints_everywhere(q4, orc):
 # products on small shapes, compared in full
 # --------------------------------------------------------------------------
 
-SHAPES = [(1, 32), (15, 64), (17, 96), (33, 256), (100, 1056), (257, 2560), (1024, 1024)]
+# at m = 2..8 the first seven take the GEMM's small-batch tiles (n <= 4096 rows),
+# the last two the block-diagonal GEMV (ragged row blocks, partial last step)
+SHAPES = [(1, 32), (15, 64), (17, 96), (33, 256), (100, 1056), (257, 2560), (1024, 1024),
+          (4097, 96), (4110, 2560)]
 
 
 def _case(orc, m, n, k, seed):
@@ -195,7 +198,9 @@ def test_blockdiag_lds_limits(q4, orc, m, n, k):
 
 SCALE_OFFSET_CASES = [("q4_gemv", 1, 1024, 37), ("q4_gemv", 2, 1024, 37),
                       ("q4_gemv", 5, 544, 37), ("q4_gemv", 8, 7936, 37),
-                      ("q4_gemv", 3, 16384, 37), ("q4_gemm", 40, 1024, 37),
+                      ("q4_gemv", 3, 16384, 37), ("q4_gemv", 2, 1024, 4099),
+                      ("q4_gemv", 8, 2560, 4099), ("q4_gemv", 5, 544, 4099),
+                      ("q4_gemm", 40, 1024, 37),
                       ("q4_gemm", 16, 1056, 37), ("q4_gemm", 32, 1056, 37),
                       ("q4_gemm", 512, 256, 4096), ("q4_gemm", 1024, 256, 4096)]
 
@@ -349,6 +354,8 @@ MULTI_SETS = [
     (7, 96, (17, 33)),                               # G = 3: partial step
     (8, 8192, (5, 61, 700)),                         # activations too large: chunked
     (3, 16384, (40, 3)),
+    (8, 2560, (4096, 4097, 1, 5000)),                # both sides of the GEMV/tile split
+    (2, 1024, (4100, 8, 4096)),
 ]
 
 
