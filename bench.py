@@ -23,8 +23,9 @@ roofline  = the dominant kernel (the 4B LM-head GEMV, m = 1, k = 2560): its
             launches over the rotated copies, after ~20 ms of untimed launches
             of the same kernel), against the 8 TB/s HBM3E peak
 gemm_m512 = the metric's second half: the M = 512 prefill GEMM (K = 2560,
-            N = 4096, activations with outlier channels), TFLOP/s against the
-            2.5 PFLOP/s dense fp16 MFMA peak
+            N = 4096, activations with outlier channels, weights rotated over
+            >= 1 GiB of copies), TFLOP/s against the 2.5 PFLOP/s dense fp16
+            MFMA peak
 detail    = every other configuration, each timed in the same run: the
             0.8B decode set and its LM head, the single 1024 x 1024 GEMV, the
             M = 16 / 128 prefill GEMMs, the M = 8 verify LM head and the
@@ -33,7 +34,8 @@ detail    = every other configuration, each timed in the same run: the
             prefill GEMM and the quantizer.  GEMMs, the verify head and the
             fp16-weight products are timed as back-to-back launches replayed
             from a HIP graph (after ~20 ms of replays), so host launch cost
-            does not pace them
+            does not pace them; every product, the GEMMs included, rotates
+            through >= 1 GiB of weight copies, so weights come from HBM
 cpu_baseline = the CPU oracle (plain C, fp64 product) on bounded row samples
             of the same configurations, GB/s over the same algorithmic bytes;
             the CPU model, the threads used, quantizer and product per
@@ -638,14 +640,17 @@ def topk_rate(torch, q4, lib, mat, m, topk, iters):
 
 def gemm_multi_rate(torch, q4, lib, mats, m, iters):
     """The projections of one prefill batch: one q4_gemm_multi launch against one
-    q4_gemm launch per matrix (weights resident; activations with outliers),
-    each replayed from a HIP graph."""
+    q4_gemm launch per matrix (weights rotated over >= ROTATE_BYTES of copies of
+    the set; activations with outliers), each replayed from a HIP graph."""
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mats[0].k, outliers=True)).cuda()
-    prods = [Product(torch, q4, mat, m, x, 1) for mat in mats]
-    multi = MultiArgs(prods, 0)
+    set_bytes = sum(mat.n * mat.k * 9 // 16 for mat in mats)
+    copies = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    prods = [Product(torch, q4, mat, m, x, copies) for mat in mats]
+    multis = [MultiArgs(prods, c) for c in range(copies)]
 
     def grouped(i, sh):
+        multi = multis[i % copies]
         st = lib.q4_gemm_multi(x.data_ptr(), m, multi.k, multi.count, multi.packed,
                                multi.scales, multi.y, multi.n, sh)
         if st != 0:
@@ -653,8 +658,9 @@ def gemm_multi_rate(torch, q4, lib, mats, m, iters):
 
     def separate(i, sh):
         for p in prods:
-            launch(lib, "q4_gemm", p.args(0), sh)
-    tg, ts = graph_time(torch, grouped, iters, 4), graph_time(torch, separate, iters, 4)
+            launch(lib, "q4_gemm", p.args(i), sh)
+    launches = max(iters, copies)
+    tg, ts = graph_time(torch, grouped, launches, 4), graph_time(torch, separate, launches, 4)
     flops = sum(p.flops for p in prods)
     del prods
     torch.cuda.empty_cache()
@@ -663,15 +669,19 @@ def gemm_multi_rate(torch, q4, lib, mats, m, iters):
             "mfma_frac_grouped": round(flops / tg / 1e12 / FP16_MFMA_PEAK_TFS, 4)}
 
 
-def gemm_case(torch, q4, lib, mat, m, outliers, iters):
+def gemm_case(torch, q4, lib, mat, m, outliers, iters, rotate=True):
     import q4_inputs as qi
     x = torch.from_numpy(qi.activations(m, mat.k, outliers=outliers)).cuda()
-    copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 9 // 16))) if m <= 8 else 1
+    # weights rotated over >= ROTATE_BYTES of copies (as for every product
+    # here): a prefill reads each layer's weights once, from HBM, not from
+    # the 256 MB Infinity Cache; the activations stay resident.  rotate=False
+    # keeps one copy (weights cache-resident), for comparison only.
+    copies = max(2, math.ceil(ROTATE_BYTES / (mat.n * mat.k * 9 // 16))) if rotate else 1
     p = Product(torch, q4, mat, m, x, copies)
     fn = "q4_gemv" if m <= 8 else "q4_gemm"
     # launches replayed from a graph, so that the host's launch cost does not
-    # pace the short GEMMs (M = 16 takes ~10 us)
-    t = graph_rate(torch, lib, fn, p, iters, 4)
+    # pace the short GEMMs (M = 16 takes ~10 us); every copy once per replay
+    t = graph_rate(torch, lib, fn, p, max(iters, copies), 4)
     out = {"matrix": mat.name, "m": m, "n": mat.n, "k": mat.k, "fn": fn, "us": round(t * 1e6, 3),
            "TFLOP_s": round(p.flops / t / 1e12, 2),
            "mfma_frac": round(p.flops / t / 1e12 / FP16_MFMA_PEAK_TFS, 4),
@@ -898,6 +908,8 @@ def main() -> int:
         log("prefill GEMM M=%d" % m)
         detail["gemm_m%d" % m] = gemm_case(torch, q4, lib, qi.PREFILL_4B, m, True, 100)
     detail["gemm_m512"] = g512
+    detail["gemm_m512_weights_cached"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100,
+                                                   rotate=False)
     log("prefill GEMM M=2048 (wide-scale weights)")
     detail["gemm_m2048"] = gemm_case(torch, q4, lib, qi.PREFILL_4B_WIDE, 2048, False, 30)
     log("verify LM head M=8 (wide-scale weights)")

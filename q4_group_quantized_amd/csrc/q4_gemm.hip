@@ -858,14 +858,16 @@ hipError_t launch_gemm32_t(const uint16_t* x, int count, const uint8_t* const* p
 // 1024, 512, 256 and 128 respectively).  All four are 32 x 32 block tiles; the
 // two smaller ones replaced 16 x 16 block tiles of the same sizes (m = 256:
 // 16.5 -> 12.4 us, m = 128: 12.5 -> 11.3 us).  The 32 x 64 tile splits K over
-// eight waves (two per SIMD) with 16-group stages in a two-stage ring: its
-// four-wave, 8-group, three-stage form waited on its loads (m = 48..128:
-// 10.6-11.0 -> 8.5-9.0 us).
+// eight waves (two per SIMD) with 16-group stages: its four-wave, 8-group,
+// three-stage form waited on its loads (m = 48..128: 10.6-11.0 -> 8.5-9.0 us
+// with cache-resident weights), and with the weights read from HBM a third
+// stage in the ring pays (m = 128: 11.3 -> 10.7 us; 8-group stages in rings
+// of 4 or 6: 12.1 / 13.1 us).
 constexpr TileChoice kTiles[] = {
     {128, 128, 35.f},      // gemm32_kernel<4, 1, 4, 2, 4, 3>: 4 column slices x 2 K phases
     {64, 128, 19.f},       // gemm32_kernel<2, 2, 2, 4, 8, 2>: 2 column slices x 4 K phases
     {64, 64, 12.5f},       // gemm32_kernel<2, 1, 2, 4, 8, 3>: 2 column slices x 4 K phases
-    {32, 64, 9.0f},        // gemm32_kernel<1, 2, 1, 8, 16, 2>: 1 column slice x 8 K phases
+    {32, 64, 9.0f},        // gemm32_kernel<1, 2, 1, 8, 16, 3>: 1 column slice x 8 K phases
 };
 
 hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* const* packed,
@@ -882,7 +884,7 @@ hipError_t launch_gemm_segments(const uint16_t* x, int count, const uint8_t* con
         case 0: return launch_gemm32_t<4, 1, 4, 2, 4, 3>(x, count, packed, scales, y, n, m, k, stream);
         case 1: return launch_gemm32_t<2, 2, 2, 4, 8, 2>(x, count, packed, scales, y, n, m, k, stream);
         case 2: return launch_gemm32_t<2, 1, 2, 4, 8, 3>(x, count, packed, scales, y, n, m, k, stream);
-        default: return launch_gemm32_t<1, 2, 1, 8, 16, 2>(x, count, packed, scales, y, n, m, k, stream);
+        default: return launch_gemm32_t<1, 2, 1, 8, 16, 3>(x, count, packed, scales, y, n, m, k, stream);
     }
 }
 
