@@ -311,7 +311,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_kernel(
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(2) * (S - 2)));
                 else
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::loads_per_stage(3) * (S - 2)));
-                barrier_keep_loads();
+                // With one column slice (WN = 1) every wave loads and reads only
+                // its own K slice's ring, so after the first stage (which also
+                // publishes the zero block) the waves need no common barrier
+                // and run apart (m = 8 / 16 at k = 2560: 3-4% faster, same bits).
+                if (WN > 1 || st == 0) barrier_keep_loads();
                 // refill the buffer computed last iteration (every wave is past it)
                 issue(st + S - 1, (u + S - 1) % S);
                 const unsigned char* sb = kbase + u * C::kStageBytes;
