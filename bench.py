@@ -882,13 +882,6 @@ def main() -> int:
     del ds["prods"], lm
     torch.cuda.empty_cache()
 
-    # ---- the metric's second half: the M = 512 prefill GEMM --------------
-    log("prefill GEMM M=512")
-    g512 = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
-    gemm_m512 = {"us": g512["us"], "TFLOP_s": g512["TFLOP_s"], "mfma_frac": g512["mfma_frac"],
-                 "peak_TFLOP_s": FP16_MFMA_PEAK_TFS,
-                 "shape": "M=512 K=2560 N=4096, x with 1% outlier channels x20"}
-
     # ---- every other configuration --------------------------------------
     log("decode set 0.8B")
     d08 = decode_set(torch, q4, lib, qi.WORKLOADS["decode_08b"], args.warmup, side, side)
@@ -907,9 +900,6 @@ def main() -> int:
     for m in (16, 128):
         log("prefill GEMM M=%d" % m)
         detail["gemm_m%d" % m] = gemm_case(torch, q4, lib, qi.PREFILL_4B, m, True, 100)
-    detail["gemm_m512"] = g512
-    detail["gemm_m512_weights_cached"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100,
-                                                   rotate=False)
     log("prefill GEMM M=2048 (wide-scale weights)")
     detail["gemm_m2048"] = gemm_case(torch, q4, lib, qi.PREFILL_4B_WIDE, 2048, False, 30)
     log("verify LM head M=8 (wide-scale weights)")
@@ -923,6 +913,20 @@ def main() -> int:
     log("grouped prefill GEMM: 4B projections, M=512")
     detail["gemm_multi_4b_proj_m512"] = gemm_multi_rate(torch, q4, lib, list(qi.DECODE_4B[:-1]),
                                                         512, 50)
+    # ---- the metric's second half: the M = 512 prefill GEMM --------------
+    # timed after every other launch of its kernel and grid (the grouped
+    # projections' separate launches at n = 4096 and the cache-resident
+    # comparison), so that its timed batch is the last of that kernel in a
+    # trace of this run
+    detail["gemm_m512_weights_cached"] = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100,
+                                                   rotate=False)
+    log("prefill GEMM M=512")
+    g512 = gemm_case(torch, q4, lib, qi.PREFILL_4B, 512, True, 100)
+    detail["gemm_m512"] = g512
+    gemm_m512 = {"us": g512["us"], "TFLOP_s": g512["TFLOP_s"], "mfma_frac": g512["mfma_frac"],
+                 "peak_TFLOP_s": FP16_MFMA_PEAK_TFS,
+                 "shape": "M=512 K=2560 N=4096, x with 1% outlier channels x20, weights "
+                          "rotated over >= 1 GiB"}
     log("fp16-weight products")
     detail["f16_gemv_lm_head_08b"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_08B[-1], 1, 60)
     detail["f16_gemv_lm_head_4b_m8"] = f16_gemv_rate(torch, q4, lib, qi.DECODE_4B[-1], 8, 30)
