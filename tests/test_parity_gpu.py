@@ -439,6 +439,7 @@ GEMM_MULTI_SETS = [
     (512, 256, (2048, 1000, 777)),                         # 64 x 128 tiles (32x32 blocks)
     (1024, 160, (4096, 130, 3000)),                        # 128 x 128 tiles, partial stage
     (3, 256, (15, 100)),                                   # m <= 8: the q4_gemv_multi path
+    (8, 1024, (4096, 4097, 17)),                           # m <= 8 on both sides of 4096 rows
 ]
 
 
